@@ -1,0 +1,120 @@
+"""ReLU-kernel linear attention with RoPE after the ReLU, fp64 (test infrastructure only).
+
+Source: SANA-Video notes, section 3.2 (the output equation and the
+``linear_attention_with_rope`` pseudocode) and section 3.4 (the causal
+equation, the constant-memory cache and Algorithm 1). Gate: the SANA-Video 2.0
+abstract and summary describe the linear layers as gated without giving the
+form; the reading is a sigmoid of a gate tensor G of O's shape, multiplied in
+after normalisation.
+
+Definition (per batch b and head h, tokens j = 1..N):
+
+    phi(x)  = max(x, 0)
+    a_i     = RoPE_i(phi(q_i)),   c_j = RoPE_j(phi(k_j))
+    KV      = sum_j c_j^T v_j                  (D x D)
+    ksum    = sum_j phi(k_j)                   (D, no RoPE)
+    o_i     = (a_i KV) / (phi(q_i) . ksum + eps)
+    o_i    <- sigmoid(g_i) * o_i               (if a gate is given)
+
+eps is added to the denominator (the equation shows none; the pseudocode adds
+it). The denominator carries no RoPE, so it is >= 0 and o_i is finite.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .rope3d import Rope3D, rope3d_angles, rope3d_rotate
+
+
+def _f64(x):
+    return None if x is None else np.asarray(x, dtype=np.float64)
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    # 1 / (1 + exp(-x)), written to avoid overflow for large |x|
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def _features(q, k, rope: Rope3D | None):
+    """phi(Q), phi(K) and their rotated forms (pseudocode steps 1 and 2)."""
+    q_relu = np.maximum(q, 0.0)
+    k_relu = np.maximum(k, 0.0)
+    if rope is None:
+        return q_relu, k_relu, q_relu, k_relu
+    if rope.n_tokens != q.shape[1]:
+        raise ValueError("RoPE grid does not match the token count")
+    theta = rope3d_angles(rope)
+    return q_relu, k_relu, rope3d_rotate(q_relu, theta), rope3d_rotate(k_relu, theta)
+
+
+def linear_attention(q, k, v, g=None, rope: Rope3D | None = None, eps: float = 1e-6,
+                     rows=None, return_state: bool = False):
+    """Bidirectional linear attention of (B, N, H, D) inputs, fp64.
+
+    ``rows`` optionally selects the token indices whose outputs are returned
+    (the state always sums over all N tokens). With ``return_state`` the
+    (KV, ksum) pair of shape (B, H, D, D) and (B, H, D) is returned as well.
+    """
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    q_relu, k_relu, q_rope, k_rope = _features(q, k, rope)
+
+    # step 3: numerator with RoPE on both sides
+    kv = np.einsum("bnhd,bnhe->bhde", k_rope, v)
+    # step 4: denominator without RoPE
+    k_sum = k_relu.sum(axis=1)
+    if rows is not None:
+        rows = np.asarray(rows)
+        q_rope, q_relu = q_rope[:, rows], q_relu[:, rows]
+        g = None if g is None else g[:, rows]
+    numerator = np.einsum("bnhd,bhde->bnhe", q_rope, kv)
+    denominator = np.einsum("bnhd,bhd->bnh", q_relu, k_sum)
+    # step 5: normalise, then gate
+    out = numerator / (denominator[..., None] + eps)
+    if g is not None:
+        out = _sigmoid(g) * out
+    if return_state:
+        return out, kv, k_sum
+    return out
+
+
+def linear_attention_chunked(q, k, v, chunk_tokens: int, g=None, rope: Rope3D | None = None,
+                             eps: float = 1e-6, kv_in=None, ksum_in=None, rows=None):
+    """Block-causal linear attention with a carried constant-memory state, fp64.
+
+    Chunk c holds tokens [c*L, min((c+1)*L, N)). Following the causal equation
+    (the own term is included) and Algorithm 1's cache update, the cache
+    (sum of states, sum of phi(K)) is advanced by each chunk in order, and the
+    chunk's tokens read the cache that already includes their own chunk:
+
+        KV_c   = KV_in   + sum_{j in chunks 0..c} c_j^T v_j
+        ksum_c = ksum_in + sum_{j in chunks 0..c} phi(k_j)
+        o_i    = (a_i KV_c(i)) / (phi(q_i) . ksum_c(i) + eps)
+
+    Returns (out, kv_out, ksum_out) with kv_out, ksum_out the cache after the
+    last chunk. ``rows`` optionally restricts the returned outputs.
+    """
+    if chunk_tokens <= 0:
+        raise ValueError("chunk_tokens must be positive")
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    B, N, H, D = q.shape
+    q_relu, k_relu, q_rope, k_rope = _features(q, k, rope)
+    kv = np.zeros((B, H, D, D)) if kv_in is None else np.array(kv_in, dtype=np.float64)
+    k_sum = np.zeros((B, H, D)) if ksum_in is None else np.array(ksum_in, dtype=np.float64)
+    out = np.zeros((B, N, H, D))
+    for start in range(0, N, chunk_tokens):
+        stop = min(N, start + chunk_tokens)
+        kv = kv + np.einsum("bnhd,bnhe->bhde", k_rope[:, start:stop], v[:, start:stop])
+        k_sum = k_sum + k_relu[:, start:stop].sum(axis=1)
+        num = np.einsum("bnhd,bhde->bnhe", q_rope[:, start:stop], kv)
+        den = np.einsum("bnhd,bhd->bnh", q_relu[:, start:stop], k_sum)
+        out[:, start:stop] = num / (den[..., None] + eps)
+    if g is not None:
+        out = _sigmoid(g) * out
+    if rows is not None:
+        out = out[:, np.asarray(rows)]
+    return out, kv, k_sum
