@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid-attention token-mixing path on one MI355X.
+
+One step is one 3:1 hybrid group at the 720p/5s latent shape (B=1, N=75600 =
+21 x 45 x 80 tokens, H=32, D=64, bf16): three gated ReLU+3D-RoPE linear
+attention layers, one gated softmax anchor and four AttnRes routes (C=2048,
+S=4 sources), every call through libhla's C ABI on one stream. Inputs are
+seeded synthetic tensors already resident in HBM.
+
+Printed: one JSON line. ``value`` is the linear-attention token throughput at
+the 720p/5s shape (tokens per second of one layer, B*N / mean layer time);
+``ms_per_step`` is the wall time of a whole group. Per-call times come from
+HIP events recorded on the stream the library launches on. ``legs`` adds the
+block-causal 720p/60s case (N=867600, chunks of 36000) timed the same way.
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the linear
+layer (a few heads) on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-legs]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
+
+
+def _dev(torch, x):
+    import numpy as np
+
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "softmax_attention_relu_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None.
+
+    profiles/hbm_traffic.txt holds one line per kernel:
+      kernel=<name> fetch_kib=<F> write_kib=<W> scale=<s> src=<sha>
+    (KiB per dispatch as the counters read them; scale turns counter KiB into
+    bytes, measured on a copy of known size). Lines whose src hash differs from
+    the current kernel source are stale and ignored.
+    """
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        kv = dict(re.findall(r"(\w+)=(\S+)", line))
+        if kv.get("kernel") == kernel and kv.get("src") == src_hash:
+            return (float(kv["fetch_kib"]) + float(kv["write_kib"])) * float(kv["scale"])
+    return None
+
+
+def cpu_baseline(heads: int):
+    """fp64 oracle on ``heads`` heads of the 720p/5s linear layer; tokens/s scaled to all 32 heads."""
+    import resource
+
+    import numpy as np
+
+    import oracle
+    import synth
+
+    w = synth.HYBRID_LINEAR[0]
+    x = w.draw()
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.perf_counter()
+    for h in range(heads):
+        f = {k: synth.to_f64(v[:, :, h:h + 1]) for k, v in x.items()}
+        oracle.linear_attention(f["q"], f["k"], f["v"], f["g"], oracle.Rope3D(w.grid), eps=w.eps)
+    wall = time.perf_counter() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    per_layer = wall * w.H / heads
+    model = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": w.B * w.N / per_layer,
+        "unit": "tokens/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle, {heads} of {w.H} heads of one 720p/5s gated linear layer "
+                  f"(N={w.N}), {wall:.1f} s wall, scaled x{w.H // heads} to the full layer",
+        "cpu_seconds": round(cpu, 2),
+        "cpu_model": model,
+        "visible_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-legs", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs the path on one GPU; --gpus above 1 is not supported "
+                                   "(the multi-GPU sharding is described in DESIGN.md)"}), flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from softmax_attention_relu_amd import hla
+
+    hla.lib()  # fails loudly if libhla.so is missing
+    torch.cuda.set_device(0)
+    dev = lambda x: _dev(torch, x)  # noqa: E731
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # ---------------- inputs, resident in HBM before timing
+    log("[bench] drawing and uploading inputs")
+    lin = []
+    for w in synth.HYBRID_LINEAR:
+        x = {k: dev(v) for k, v in w.draw().items()}
+        x["o"] = torch.empty_like(x["q"])
+        x["rope"] = hla.Rope3D(w.grid, w.bands, w.base)
+        x["ws"] = torch.empty(hla.hla_linear_attn_workspace(w.B, w.N, w.H, w.D), dtype=torch.uint8, device="cuda")
+        lin.append((w, x))
+    aw = synth.HYBRID_ANCHOR
+    anc = {k: dev(v) for k, v in aw.draw().items()}
+    anc["o"] = torch.empty_like(anc["q"])
+    anc["ws"] = torch.empty(hla.hla_softmax_anchor_workspace(aw.B, aw.N, aw.H, aw.D), dtype=torch.uint8,
+                            device="cuda")
+    routes = []
+    for rw in synth.HYBRID_ROUTES:
+        r = rw.draw()
+        rr = {"v": [dev(s) for s in r["v"]], "w": dev(r["w"]), "phi": dev(r["phi_t"])}
+        rr["h"] = torch.empty_like(rr["v"][0])
+        routes.append((rw, rr))
+    torch.cuda.synchronize()
+
+    names = [f"linear{i}" for i in range(3)] + ["anchor"] + [f"route{i}" for i in range(4)]
+
+    def step(ev=None):
+        # hybrid group in model order: route -> mixer, three linear layers then the anchor
+        for i in range(4):
+            rw, rr = routes[i]
+            if ev is not None:
+                ev[f"route{i}"][0].record()
+            hla.hla_attnres_route(rr["v"], rr["w"], rr["phi"], rw.eps, h=rr["h"])
+            if ev is not None:
+                ev[f"route{i}"][1].record()
+            if i < 3:
+                w, x = lin[i]
+                if ev is not None:
+                    ev[f"linear{i}"][0].record()
+                hla.hla_linear_attn(x["q"], x["k"], x["v"], x["g"], x["rope"], w.eps, o=x["o"], ws=x["ws"])
+                if ev is not None:
+                    ev[f"linear{i}"][1].record()
+            else:
+                if ev is not None:
+                    ev["anchor"][0].record()
+                hla.hla_softmax_anchor(anc["q"], anc["k"], anc["v"], anc["g"], aw.scale, o=anc["o"], ws=anc["ws"])
+                if ev is not None:
+                    ev["anchor"][1].record()
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    per = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
+    log("[bench] per-call ms: " + ", ".join(f"{n} {v:.3f}" for n, v in per.items()))
+
+    w0 = synth.HYBRID_LINEAR[0]
+    tokh = w0.B * w0.N * w0.H
+    lin_ms = float(np.mean([per[f"linear{i}"] for i in range(3)]))
+    lin_bytes = tokh * 64 * 2 * 5  # Q, K, V, G read + O written, bf16
+    lin_gbs = lin_bytes / (lin_ms * 1e-3) / 1e9
+    anc_ms = per["anchor"]
+    anc_flops = 4.0 * aw.B * aw.H * aw.N * aw.N * aw.D
+    anc_tflops = anc_flops / (anc_ms * 1e-3) / 1e12
+    rt_ms = float(np.mean([per[f"route{i}"] for i in range(4)]))
+    rw0 = synth.HYBRID_ROUTES[0]
+    rt_bytes = rw0.B * rw0.T * rw0.C * 2 * (rw0.S + 1)
+    rt_gbs = rt_bytes / (rt_ms * 1e-3) / 1e9
+
+    anchor_traffic = _traffic("anchor_fwd_kernel", _src_hash("anchor.hip"))
+    out = {
+        "metric": "linear-attn tokens/s & HBM GB/s at 720p/5s shape; anchor MFMA util %",
+        "value": w0.B * w0.N / (lin_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 tensors; router queries N(0,0.02^2) fp32)",
+        "config": {"workload": "hybrid 3:1 group at 720p/5s: 3 gated linear layers + 1 gated softmax anchor "
+                               "+ 4 AttnRes routes", "B": 1, "N": 75600, "grid": [21, 45, 80], "H": 32, "D": 64,
+                   "route_C": 2048, "route_S": 4, "parallelism": "single GPU"},
+        "linear_hbm_gbs": lin_gbs,
+        "linear_hbm_frac": lin_gbs / HBM_PEAK_GBS,
+        "linear_ms": lin_ms,
+        "anchor_mfma_util_pct": 100.0 * anc_tflops / BF16_PEAK_TFLOPS,
+        "anchor_ms": anc_ms,
+        "route_hbm_gbs": rt_gbs,
+        "route_ms": rt_ms,
+        "per_call_ms": per,
+        "roofline": {"bound": "mfma", "kernel": "anchor_fwd_kernel (call incl. V-transpose pre-pass)",
+                     "achieved": anc_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": anc_tflops / BF16_PEAK_TFLOPS, "traffic": anchor_traffic},
+        "rooflines": {
+            "linear_attn": {"bound": "hbm", "achieved": lin_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": lin_gbs / HBM_PEAK_GBS, "algorithmic_bytes": lin_bytes},
+            "attnres_route": {"bound": "hbm", "achieved": rt_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": rt_gbs / HBM_PEAK_GBS, "algorithmic_bytes": rt_bytes},
+        },
+    }
+
+    # ---------------- block-causal 720p/60s leg
+    if not args.no_legs:
+        del lin, routes
+        torch.cuda.empty_cache()
+        cw = synth.CHUNKED_720P60S
+        log("[bench] chunked 720p/60s leg: drawing inputs")
+        cx = {k: dev(v) for k, v in cw.draw().items()}
+        cx["o"] = torch.empty_like(cx["q"])
+        rope = hla.Rope3D(cw.grid, cw.bands, cw.base)
+        ws = torch.empty(hla.hla_linear_attn_chunked_workspace(cw.B, cw.N, cw.H, cw.D, cw.chunk_tokens),
+                         dtype=torch.uint8, device="cuda")
+        kv = torch.zeros((cw.B, cw.H, 64, 64), dtype=torch.float32, device="cuda")
+        ks = torch.zeros((cw.B, cw.H, 64), dtype=torch.float32, device="cuda")
+
+        def call():
+            hla.hla_linear_attn_chunked(cx["q"], cx["k"], cx["v"], cw.chunk_tokens, None, rope, cw.eps,
+                                        kv_out=kv, ksum_out=ks, o=cx["o"], ws=ws)
+
+        call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        c_ms = float(np.mean(times))
+        c_bytes = cw.B * cw.N * cw.H * 64 * 2 * 4  # Q, K, V read + O written
+        out["legs"] = {"chunked_720p60s": {
+            "N": cw.N, "chunk_tokens": cw.chunk_tokens, "ms": c_ms, "tokens_per_s": cw.B * cw.N / (c_ms * 1e-3),
+            "hbm_gbs": c_bytes / (c_ms * 1e-3) / 1e9, "hbm_frac": c_bytes / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": c_bytes}}
+        log(f"[bench] chunked: {c_ms:.3f} ms")
+        del cx, ws
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_heads} heads")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_heads)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,176 @@
+/*
+ * libhla -- token-mixing path of the SANA-Video / SANA-Video 2.0 hybrid
+ * attention layer, for AMD Instinct MI355X (gfx950).
+ *
+ * Four operations, each a set of hand-written HIP kernels:
+ *
+ *   hla_linear_attn          bidirectional ReLU-kernel linear attention with 3D
+ *                            RoPE after the ReLU, a RoPE-free denominator and an
+ *                            optional sigmoid output gate.
+ *   hla_linear_attn_chunked  block-causal variant that carries the cumulative
+ *                            D x D state and key sum across chunks.
+ *   hla_softmax_anchor       gated non-causal softmax attention (the periodic
+ *                            full-rank anchor layer).
+ *   hla_attnres_route        block attention-residual (AttnRes) depth router.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Ownership: the caller allocates and owns every buffer. Tensor pointers are
+ *   DEVICE pointers to contiguous memory in the layouts stated per call; the
+ *   hla_rope3d struct and the array of source pointers of the router are HOST
+ *   memory that is read during the call only. The library never allocates,
+ *   frees or synchronises, and keeps no pointer after it returns.
+ * - Asynchrony: every call enqueues its kernels on `stream` (NULL = the
+ *   default stream) and returns; outputs are valid once the stream has
+ *   executed them.
+ * - Errors: arguments are validated before anything is launched. A rejected
+ *   call returns HLA_ERR_INVALID_ARG, HLA_ERR_UNSUPPORTED or HLA_ERR_WORKSPACE
+ *   and has no side effect. A failed launch returns HLA_ERR_HIP. No C++
+ *   exception crosses this interface. The library holds no mutable global
+ *   state, so calls from several host threads are safe.
+ * - Aliasing: outputs must not overlap inputs, except kv_out == kv_in and
+ *   ksum_out == ksum_in in hla_linear_attn_chunked.
+ * - Numbers: HLA_BF16 tensors hold bfloat16 values, HLA_F32 tensors float.
+ *   States, key sums, router queries and RoPE tables are always float.
+ *   Arithmetic is float32 throughout; bf16 outputs are rounded to nearest
+ *   even. Only head dimension D = 64 is built.
+ * - Determinism: no floating-point atomics are used; a call repeated on the
+ *   same inputs returns bitwise identical outputs.
+ */
+#ifndef HLA_H
+#define HLA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HLA_OK = 0,
+  HLA_ERR_INVALID_ARG = 1, /* null required pointer, bad size, inconsistent shapes */
+  HLA_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (D != 64, ...) */
+  HLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace query */
+  HLA_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError) */
+} hla_status;
+
+typedef enum { HLA_BF16 = 0, HLA_F32 = 1 } hla_dtype;
+
+/*
+ * 3D rotary position embedding (SANA-Video notes, section 3.2 and Figure 2(c):
+ * RoPE is applied to the ReLU features of Q and K). The pages do not define the
+ * rotation; this library uses the following reading:
+ *   token n of a call sits at frame t, row y, column x of a grid_t x grid_h x
+ *   grid_w latent grid, n = (t * grid_h + y) * grid_w + x (t-major);
+ *   dims [0, d_t) rotate with t, [d_t, d_t + d_h) with y, the rest with x;
+ *   inside a band, adjacent pairs (2k, 2k+1) rotate by the angle a_k of the
+ *   token's coordinate: (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
+ * The tables hold (cos a, sin a) as float pairs, row r for coordinate r:
+ *   cs_t: [grid_t][d_t/2][2], cs_h: [grid_h][d_h/2][2], cs_w: [grid_w][d_w/2][2].
+ * hla_rope_table_host fills one table; a streaming caller whose first frame is
+ * global frame t0 builds cs_t with pos0 = t0.
+ */
+typedef struct {
+  int grid_t, grid_h, grid_w; /* grid_t * grid_h * grid_w must equal N */
+  int d_t, d_h, d_w;          /* even, d_t + d_h + d_w == D */
+  const float *cs_t;          /* device */
+  const float *cs_h;          /* device */
+  const float *cs_w;          /* device */
+} hla_rope3d;
+
+/*
+ * Host helper: out[r][k] = (cos a, sin a), a = (pos0 + r) * base^(-2k / d_band),
+ * for r in [0, len) and k in [0, d_band/2). Angles are formed in double and
+ * rounded to float. `out` is HOST memory of len * d_band floats.
+ * Errors: INVALID_ARG if out is NULL, len <= 0, d_band <= 0 or odd, base <= 0.
+ */
+hla_status hla_rope_table_host(int len, int pos0, int d_band, double base, float *out);
+
+/*
+ * Bidirectional ReLU-kernel linear attention with RoPE after the ReLU
+ * (SANA-Video notes, section 3.2: output equation and pseudocode), with an
+ * optional output gate (SANA-Video 2.0 abstract: the linear layers are gated;
+ * form read as sigmoid(G) times the normalised output). Per batch b, head h:
+ *   a_i = RoPE_i(relu(q_i)),  c_j = RoPE_j(relu(k_j))
+ *   KV  = sum_j c_j^T v_j (D x D),   z = sum_j relu(k_j)  (no RoPE)
+ *   o_i = (a_i KV) / (relu(q_i) . z + eps),  then o_i *= sigmoid(g_i) if g
+ * q, k, v, g, o: [B][N][H][D] of dtype `dt` (token-major, head, then dim).
+ * g may be NULL (no gate); rope may be NULL (no rotation).
+ * ws: device workspace of at least hla_linear_attn_workspace(B, N, H, D) bytes
+ *     (its contents on entry do not matter and are overwritten).
+ * Errors: INVALID_ARG for null q/k/v/o, B, N or H <= 0, bad rope fields or a
+ * rope grid whose product differs from N; UNSUPPORTED for D != 64 or an
+ * unknown dtype; WORKSPACE if ws is NULL or ws_bytes is too small.
+ */
+size_t hla_linear_attn_workspace(int B, int N, int H, int D);
+hla_status hla_linear_attn(hla_dtype dt, int B, int N, int H, int D,
+                           const void *q, const void *k, const void *v, const void *g,
+                           const hla_rope3d *rope, float eps,
+                           void *o, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Block-causal linear attention with a constant-memory carried state
+ * (SANA-Video notes, section 3.4: causal equation with the own term included,
+ * the cache of cumulative states and key sums, and Algorithm 1's update).
+ * Chunk c holds tokens [c L, min((c+1) L, N)), L = chunk_tokens; the last chunk
+ * may be shorter. With P_c = KV_in + sum of c_j^T v_j over chunks 0..c and
+ * Z_c = z_in + sum of relu(k_j) over chunks 0..c, token i of chunk c gets
+ *   o_i = (a_i P_c) / (relu(q_i) . Z_c + eps),  then the optional gate.
+ * kv_in [B][H][D][D] and ksum_in [B][H][D] (float, device) may both be NULL
+ * for a zero state; kv_out and ksum_out receive P_last and Z_last and may both
+ * be NULL (the call then does not commit its state). kv_out may equal kv_in and
+ * ksum_out may equal ksum_in. Other arguments as hla_linear_attn; the rope
+ * grid covers the N tokens of this call.
+ * Errors: as hla_linear_attn, plus INVALID_ARG for chunk_tokens <= 0 or only one
+ * of each in/out pair given.
+ */
+size_t hla_linear_attn_chunked_workspace(int B, int N, int H, int D, int chunk_tokens);
+hla_status hla_linear_attn_chunked(hla_dtype dt, int B, int N, int H, int D, int chunk_tokens,
+                                   const void *q, const void *k, const void *v, const void *g,
+                                   const hla_rope3d *rope, float eps,
+                                   const float *kv_in, const float *ksum_in,
+                                   float *kv_out, float *ksum_out,
+                                   void *o, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gated non-causal softmax attention, the anchor layer of the 3:1 hybrid
+ * (SANA-Video 2.0 abstract and summary; textbook scaled dot-product form):
+ *   o_i = sigmoid(g_i) * sum_j softmax_j(scale * q_i . k_j) v_j
+ * q, k, v, g, o: [B][N][H][D] bf16 (dt must be HLA_BF16); g may be NULL.
+ * Products run on bf16 matrix cores with float accumulation and a float
+ * online softmax; the probabilities are rounded to bf16 for the P.V product.
+ * ws: device workspace of at least hla_softmax_anchor_workspace(B, N, H, D)
+ *     bytes; it receives V transposed per head (contents on entry ignored).
+ * Errors: INVALID_ARG for null q/k/v/o, B, N or H <= 0, scale not finite and
+ * positive; UNSUPPORTED for D != 64 or dt != HLA_BF16; WORKSPACE if ws is NULL
+ * or ws_bytes is too small.
+ */
+size_t hla_softmax_anchor_workspace(int B, int N, int H, int D);
+hla_status hla_softmax_anchor(hla_dtype dt, int B, int N, int H, int D,
+                              const void *q, const void *k, const void *v, const void *g,
+                              float scale, void *o, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Block attention-residual router (SANA-Video 2.0 summary, method section,
+ * router equation). For each of the B*T tokens, with u_b = w + phi_t[b]:
+ *   l_i = u_b . RMSNorm(v_i),  RMSNorm(v) = v / sqrt(mean_c v_c^2 + eps)
+ *   alpha = softmax_i(l),      h = sum_i alpha_i v_i   (raw sources)
+ * v: HOST array of S device pointers, each [B][T][C] of dtype dt.
+ * w: [C] float; phi_t: [B][C] float or NULL (router without timestep).
+ * h: [B][T][C] of dtype dt; alpha: [B][T][S] float or NULL.
+ * Errors: INVALID_ARG for null v, v[i], w or h, B, T or C <= 0, C % 8 != 0,
+ * S outside [1, 16]; UNSUPPORTED for C > 4096 or an unknown dtype.
+ */
+hla_status hla_attnres_route(hla_dtype dt, int B, int T, int C, int S,
+                             const void *const *v, const float *w, const float *phi_t, float eps,
+                             void *h, float *alpha, hipStream_t stream);
+
+/* Static description of a status code; never NULL. */
+const char *hla_status_string(hla_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLA_H */

@@ -1,0 +1,65 @@
+"""Compile libhla.so for gfx950 in-tree with hipcc.
+
+    python -m softmax_attention_relu_amd.build
+
+Each source compiles to an object in ``_build/`` (parallel hipcc processes),
+then one link produces ``softmax_attention_relu_amd/libhla.so``.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libhla.so")
+SOURCES = ["hla_api.cpp", "linear_attn.hip", "anchor.hip", "route.hip"]
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # never form packed-fp32 VALU ops (v_pk_{add,mul,fma}_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def _compile(src: str, extra) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd[1:1] = ["-x", "hip"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in r.stderr.splitlines() if ln.strip() and noise not in ln]
+    if msgs:
+        sys.stderr.write("\n".join(msgs) + "\n")
+    return obj
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
+    tmp = LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    extra = sys.argv[1:]
+    build(verbose=True, extra=extra)

@@ -1,0 +1,90 @@
+// Device-side helpers for gfx950: vector types for the matrix cores, bf16
+// packing, fast division and the RoPE table lookup.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hla_internal.h"
+
+namespace hla {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// bf16 lives in memory as 16-bit patterns; two of them per 32-bit word,
+// element 2i in the low half (little endian).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to bf16 (nearest even, v_cvt_pk_bf16_f32) and pack them.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2_t x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+}
+
+// Low / high 16-bit halves of two words packed into one word.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv &f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// One rotated pair: which band table it reads and where its column starts.
+struct RopePair {
+  const float *col;  // table + 2 * k (k = pair index inside its band)
+  int stride;        // floats per table row (= band width)
+  int band;          // 0: t, 1: y, 2: x
+};
+
+__device__ __forceinline__ RopePair rope_pair(const RopeArgs &r, int p) {
+  RopePair rp;
+  const int two_p = 2 * p;
+  if (two_p < r.d_t) {
+    rp.col = r.cs_t + two_p;
+    rp.stride = r.d_t;
+    rp.band = 0;
+  } else if (two_p < r.d_t + r.d_h) {
+    rp.col = r.cs_h + (two_p - r.d_t);
+    rp.stride = r.d_h;
+    rp.band = 1;
+  } else {
+    rp.col = r.cs_w + (two_p - r.d_t - r.d_h);
+    rp.stride = r.d_w;
+    rp.band = 2;
+  }
+  return rp;
+}
+
+struct TokenPos {
+  uint32_t t, y, x;
+};
+
+__device__ __forceinline__ TokenPos token_pos(const RopeArgs &r, uint32_t n) {
+  TokenPos p;
+  p.t = fast_div(n, r.div_hw);
+  const uint32_t rem = n - p.t * r.hw;
+  p.y = fast_div(rem, r.div_w);
+  p.x = rem - p.y * r.w;
+  return p;
+}
+
+// (cos, sin) of pair `rp` at token position `tp`.
+__device__ __forceinline__ f32x2_t rope_cs(const RopePair &rp, const TokenPos &tp) {
+  const uint32_t pos = rp.band == 0 ? tp.t : (rp.band == 1 ? tp.y : tp.x);
+  return *reinterpret_cast<const f32x2_t *>(rp.col + (size_t)pos * rp.stride);
+}
+
+// Rotate (x0, x1) by the angle whose (cos, sin) is cs.
+__device__ __forceinline__ void rotate(float &x0, float &x1, f32x2_t cs) {
+  const float a = x0 * cs.x - x1 * cs.y;
+  const float b = x0 * cs.y + x1 * cs.x;
+  x0 = a;
+  x1 = b;
+}
+
+}  // namespace hla

@@ -1,0 +1,186 @@
+// C-ABI entry points of libhla: argument validation (before any launch),
+// workspace sizing, the RoPE table helper, and dispatch to the kernel files.
+#include <math.h>
+#include <string.h>
+
+#include "hla_internal.h"
+
+using namespace hla;
+
+namespace {
+
+bool rope_valid(const hla_rope3d *r, int N, int D) {
+  if (!r) return true;
+  if (r->grid_t <= 0 || r->grid_h <= 0 || r->grid_w <= 0) return false;
+  if ((long long)r->grid_t * r->grid_h * r->grid_w != (long long)N) return false;
+  if (r->d_t < 0 || r->d_h < 0 || r->d_w < 0) return false;
+  if ((r->d_t | r->d_h | r->d_w) & 1) return false;
+  if (r->d_t + r->d_h + r->d_w != D) return false;
+  if ((r->d_t && !r->cs_t) || (r->d_h && !r->cs_h) || (r->d_w && !r->cs_w)) return false;
+  return true;
+}
+
+RopeArgs make_rope(const hla_rope3d *r) {
+  RopeArgs ra;
+  memset(&ra, 0, sizeof(ra));
+  if (!r) return ra;
+  ra.enabled = 1;
+  ra.d_t = r->d_t;
+  ra.d_h = r->d_h;
+  ra.d_w = r->d_w;
+  ra.hw = (uint32_t)r->grid_h * (uint32_t)r->grid_w;
+  ra.w = (uint32_t)r->grid_w;
+  ra.div_hw = make_fastdiv(ra.hw);
+  ra.div_w = make_fastdiv(ra.w);
+  ra.cs_t = r->cs_t;
+  ra.cs_h = r->cs_h;
+  ra.cs_w = r->cs_w;
+  return ra;
+}
+
+bool shape_ok(int B, int N, int H) {
+  if (B <= 0 || N <= 0 || H <= 0) return false;
+  // every element offset of a [B][N][H][64] tensor fits in 63 bits and every
+  // token index in 31 bits; grid dimensions fit in 31 bits
+  if ((long long)B * H > (1LL << 30)) return false;
+  return true;
+}
+
+hla_status linear_common(hla_dtype dt, int B, int N, int H, int D, int chunk_tokens, const void *q, const void *k,
+                         const void *v, const void *g, const hla_rope3d *rope, float eps, const float *kv_in,
+                         const float *ksum_in, float *kv_out, float *ksum_out, void *o, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (!q || !k || !v || !o) return HLA_ERR_INVALID_ARG;
+  if (!shape_ok(B, N, H) || chunk_tokens <= 0) return HLA_ERR_INVALID_ARG;
+  if ((kv_in == nullptr) != (ksum_in == nullptr)) return HLA_ERR_INVALID_ARG;
+  if ((kv_out == nullptr) != (ksum_out == nullptr)) return HLA_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || isinf(eps)) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16 && dt != HLA_F32) return HLA_ERR_UNSUPPORTED;
+  if (D != kD) return HLA_ERR_UNSUPPORTED;
+  if (!rope_valid(rope, N, D)) return HLA_ERR_INVALID_ARG;
+  const LinearPlan plan = plan_linear(B, N, H, chunk_tokens);
+  if (!ws || ws_bytes < plan.total_bytes) return HLA_ERR_WORKSPACE;
+  LinearArgs a;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.o = o;
+  a.rope = make_rope(rope);
+  a.eps = eps;
+  a.kv_in = kv_in;
+  a.ksum_in = ksum_in;
+  a.kv_out = kv_out;
+  a.ksum_out = ksum_out;
+  a.ws = ws;
+  return launch_linear(dt, a, plan, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+hla_status hla_rope_table_host(int len, int pos0, int d_band, double base, float *out) {
+  if (!out || len <= 0 || d_band <= 0 || (d_band & 1) || !(base > 0.0)) return HLA_ERR_INVALID_ARG;
+  const int half = d_band / 2;
+  for (int r = 0; r < len; ++r) {
+    const double p = (double)pos0 + (double)r;
+    for (int k = 0; k < half; ++k) {
+      const double a = p * pow(base, -2.0 * (double)k / (double)d_band);
+      out[((size_t)r * half + k) * 2] = (float)cos(a);
+      out[((size_t)r * half + k) * 2 + 1] = (float)sin(a);
+    }
+  }
+  return HLA_OK;
+}
+
+size_t hla_linear_attn_workspace(int B, int N, int H, int D) {
+  if (!shape_ok(B, N, H) || D != kD) return 0;
+  return plan_linear(B, N, H, N).total_bytes;
+}
+
+hla_status hla_linear_attn(hla_dtype dt, int B, int N, int H, int D, const void *q, const void *k, const void *v,
+                           const void *g, const hla_rope3d *rope, float eps, void *o, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  return linear_common(dt, B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, nullptr, nullptr, o,
+                       ws, ws_bytes, stream);
+}
+
+size_t hla_linear_attn_chunked_workspace(int B, int N, int H, int D, int chunk_tokens) {
+  if (!shape_ok(B, N, H) || D != kD || chunk_tokens <= 0) return 0;
+  return plan_linear(B, N, H, chunk_tokens).total_bytes;
+}
+
+hla_status hla_linear_attn_chunked(hla_dtype dt, int B, int N, int H, int D, int chunk_tokens, const void *q,
+                                   const void *k, const void *v, const void *g, const hla_rope3d *rope, float eps,
+                                   const float *kv_in, const float *ksum_in, float *kv_out, float *ksum_out, void *o,
+                                   void *ws, size_t ws_bytes, hipStream_t stream) {
+  return linear_common(dt, B, N, H, D, chunk_tokens, q, k, v, g, rope, eps, kv_in, ksum_in, kv_out, ksum_out, o, ws,
+                       ws_bytes, stream);
+}
+
+size_t hla_softmax_anchor_workspace(int B, int N, int H, int D) {
+  if (!shape_ok(B, N, H) || D != kD) return 0;
+  return anchor_workspace_bytes(B, N, H);
+}
+
+hla_status hla_softmax_anchor(hla_dtype dt, int B, int N, int H, int D, const void *q, const void *k, const void *v,
+                              const void *g, float scale, void *o, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o) return HLA_ERR_INVALID_ARG;
+  if (!shape_ok(B, N, H) || !isfinite(scale) || !(scale > 0.f)) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < anchor_workspace_bytes(B, N, H)) return HLA_ERR_WORKSPACE;
+  AnchorArgs a;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.o = o;
+  a.scale = scale;
+  a.ws = ws;
+  return launch_anchor(a, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
+}
+
+hla_status hla_attnres_route(hla_dtype dt, int B, int T, int C, int S, const void *const *v, const float *w,
+                             const float *phi_t, float eps, void *h, float *alpha, hipStream_t stream) {
+  if (!v || !w || !h) return HLA_ERR_INVALID_ARG;
+  if (B <= 0 || T <= 0 || C <= 0 || (C % 8) != 0 || S < 1 || S > kMaxSources) return HLA_ERR_INVALID_ARG;
+  if ((long long)B * T > (1LL << 31) - 1) return HLA_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || isinf(eps)) return HLA_ERR_INVALID_ARG;
+  for (int i = 0; i < S; ++i)
+    if (!v[i]) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16 && dt != HLA_F32) return HLA_ERR_UNSUPPORTED;
+  if (C > 4096) return HLA_ERR_UNSUPPORTED;
+  RouteArgs a;
+  memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.T = T;
+  a.C = C;
+  a.S = S;
+  for (int i = 0; i < S; ++i) a.v[i] = v[i];
+  a.w = w;
+  a.phi_t = phi_t;
+  a.eps = eps;
+  a.h = h;
+  a.alpha = alpha;
+  return launch_route(dt, a, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
+}
+
+const char *hla_status_string(hla_status s) {
+  switch (s) {
+    case HLA_OK: return "HLA_OK";
+    case HLA_ERR_INVALID_ARG: return "HLA_ERR_INVALID_ARG: invalid argument";
+    case HLA_ERR_UNSUPPORTED: return "HLA_ERR_UNSUPPORTED: unsupported dtype or head dimension";
+    case HLA_ERR_WORKSPACE: return "HLA_ERR_WORKSPACE: workspace missing or too small";
+    case HLA_ERR_HIP: return "HLA_ERR_HIP: kernel launch failed";
+  }
+  return "HLA_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,266 @@
+"""Thin Python binding of libhla (ctypes).
+
+Argument marshalling only: every step of every operation runs in the HIP
+kernels of ``libhla.so``. PyTorch is used for device memory and the current
+HIP stream. The functions carry the C entry points' names; tensors are
+contiguous device tensors of shape (B, N, H, 64) (bf16, or float32 for the
+linear paths), state tensors are float32.
+
+If ``libhla.so`` has not been built, ``lib()`` raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_double, c_float, c_int, c_size_t, c_void_p
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhla.so")
+
+HLA_OK, HLA_ERR_INVALID_ARG, HLA_ERR_UNSUPPORTED, HLA_ERR_WORKSPACE, HLA_ERR_HIP = range(5)
+HLA_BF16, HLA_F32 = 0, 1
+
+# every function declared in include/hla.h
+EXPORTS = (
+    "hla_rope_table_host",
+    "hla_linear_attn_workspace",
+    "hla_linear_attn",
+    "hla_linear_attn_chunked_workspace",
+    "hla_linear_attn_chunked",
+    "hla_softmax_anchor_workspace",
+    "hla_softmax_anchor",
+    "hla_attnres_route",
+    "hla_status_string",
+)
+
+
+class HlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {hla_status_string(status)} (status {status})")
+
+
+class hla_rope3d(ctypes.Structure):
+    _fields_ = [
+        ("grid_t", c_int), ("grid_h", c_int), ("grid_w", c_int),
+        ("d_t", c_int), ("d_h", c_int), ("d_w", c_int),
+        ("cs_t", c_void_p), ("cs_h", c_void_p), ("cs_w", c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhla.so (once). Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m softmax_attention_relu_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.hla_rope_table_host.argtypes = [c_int, c_int, c_int, c_double, POINTER(c_float)]
+        L.hla_rope_table_host.restype = c_int
+        L.hla_linear_attn_workspace.argtypes = [c_int, c_int, c_int, c_int]
+        L.hla_linear_attn_workspace.restype = c_size_t
+        L.hla_linear_attn.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      POINTER(hla_rope3d), c_float, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.hla_linear_attn.restype = c_int
+        L.hla_linear_attn_chunked_workspace.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        L.hla_linear_attn_chunked_workspace.restype = c_size_t
+        L.hla_linear_attn_chunked.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, POINTER(hla_rope3d), c_float, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.hla_linear_attn_chunked.restype = c_int
+        L.hla_softmax_anchor_workspace.argtypes = [c_int, c_int, c_int, c_int]
+        L.hla_softmax_anchor_workspace.restype = c_size_t
+        L.hla_softmax_anchor.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_float, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.hla_softmax_anchor.restype = c_int
+        L.hla_attnres_route.argtypes = [c_int, c_int, c_int, c_int, c_int, POINTER(c_void_p), c_void_p, c_void_p,
+                                        c_float, c_void_p, c_void_p, c_void_p]
+        L.hla_attnres_route.restype = c_int
+        L.hla_status_string.argtypes = [c_int]
+        L.hla_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def hla_status_string(status: int) -> str:
+    return lib().hla_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != HLA_OK:
+        raise HlaError(status, where)
+
+
+# ----------------------------------------------------------------------------
+# torch marshalling helpers
+
+def _torch():
+    import torch  # imported lazily so host-only users do not need a GPU
+
+    return torch
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("libhla takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libhla takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return HLA_BF16
+    if t.dtype == torch.float32:
+        return HLA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> int | None:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _bnhd(q):
+    if q.dim() != 4:
+        raise ValueError("expected a (B, N, H, D) tensor")
+    return tuple(int(x) for x in q.shape)
+
+
+def _workspace(nbytes: int, device, ws):
+    torch = _torch()
+    if ws is None:
+        ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+# ----------------------------------------------------------------------------
+# RoPE tables
+
+def hla_rope_table_host(length: int, pos0: int, d_band: int, base: float = 10000.0) -> np.ndarray:
+    """(cos, sin) table of one band: float32 array of shape (length, d_band/2, 2)."""
+    out = np.zeros((max(int(length), 0), max(int(d_band), 0) // 2, 2), dtype=np.float32)
+    ptr = out.ctypes.data_as(POINTER(c_float)) if out.size else POINTER(c_float)()
+    _check(lib().hla_rope_table_host(int(length), int(pos0), int(d_band), float(base), ptr), "hla_rope_table_host")
+    return out
+
+
+class Rope3D:
+    """Device RoPE tables for a (T, Hg, Wg) grid; the t table starts at frame ``t_offset``."""
+
+    def __init__(self, grid, bands=(16, 24, 24), base: float = 10000.0, t_offset: int = 0, device="cuda",
+                 tables=None):
+        torch = _torch()
+        self.grid = tuple(int(x) for x in grid)
+        self.bands = tuple(int(x) for x in bands)
+        if tables is None:
+            pos0 = (int(t_offset), 0, 0)
+            tables = [hla_rope_table_host(n, p, d, base) if d > 0 else np.zeros((1, 1, 2), np.float32)
+                      for n, p, d in zip(self.grid, pos0, self.bands)]
+        self.tables = [torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).to(device) for t in tables]
+        s = hla_rope3d()
+        s.grid_t, s.grid_h, s.grid_w = self.grid
+        s.d_t, s.d_h, s.d_w = self.bands
+        s.cs_t, s.cs_h, s.cs_w = (t.data_ptr() for t in self.tables)
+        self._struct = s
+
+    def struct(self) -> hla_rope3d:
+        return self._struct
+
+
+def _rope_ptr(rope):
+    return None if rope is None else ctypes.byref(rope.struct())
+
+
+# ----------------------------------------------------------------------------
+# entry points
+
+def hla_linear_attn_workspace(B: int, N: int, H: int, D: int = 64) -> int:
+    return int(lib().hla_linear_attn_workspace(B, N, H, D))
+
+
+def hla_linear_attn(q, k, v, g=None, rope: Rope3D | None = None, eps: float = 1e-6, o=None, ws=None, stream=None):
+    """Bidirectional ReLU+RoPE linear attention; returns o."""
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    if o is None:
+        o = torch.empty_like(q)
+    ws, nbytes = _workspace(hla_linear_attn_workspace(B, N, H, D), q.device, ws)
+    st = lib().hla_linear_attn(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _rope_ptr(rope),
+                               float(eps), _ptr(o), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_linear_attn")
+    return o
+
+
+def hla_linear_attn_chunked_workspace(B: int, N: int, H: int, D: int, chunk_tokens: int) -> int:
+    return int(lib().hla_linear_attn_chunked_workspace(B, N, H, D, chunk_tokens))
+
+
+def hla_linear_attn_chunked(q, k, v, chunk_tokens: int, g=None, rope: Rope3D | None = None, eps: float = 1e-6,
+                            kv_in=None, ksum_in=None, kv_out=None, ksum_out=None, o=None, ws=None, stream=None):
+    """Block-causal linear attention with carried state; returns o (state goes to kv_out/ksum_out)."""
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    if o is None:
+        o = torch.empty_like(q)
+    ws, nbytes = _workspace(hla_linear_attn_chunked_workspace(B, N, H, D, chunk_tokens), q.device, ws)
+    st = lib().hla_linear_attn_chunked(_dtype_code(q), B, N, H, D, int(chunk_tokens), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(g), _rope_ptr(rope), float(eps), _ptr(kv_in), _ptr(ksum_in),
+                                       _ptr(kv_out), _ptr(ksum_out), _ptr(o), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_linear_attn_chunked")
+    return o
+
+
+def hla_softmax_anchor_workspace(B: int, N: int, H: int, D: int = 64) -> int:
+    return int(lib().hla_softmax_anchor_workspace(B, N, H, D))
+
+
+def hla_softmax_anchor(q, k, v, g=None, scale: float | None = None, o=None, ws=None, stream=None):
+    """Gated non-causal softmax attention (bf16); returns o."""
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if o is None:
+        o = torch.empty_like(q)
+    ws, nbytes = _workspace(hla_softmax_anchor_workspace(B, N, H, D), q.device, ws)
+    st = lib().hla_softmax_anchor(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
+                                  _ptr(o), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_softmax_anchor")
+    return o
+
+
+def hla_attnres_route(sources, w, phi_t=None, eps: float = 1e-6, h=None, alpha=None, stream=None):
+    """AttnRes router over S sources of shape (B, T, C); returns (h, alpha).
+
+    ``alpha`` may be a float32 (B, T, S) tensor to fill, True to allocate one,
+    or None to skip the routing-weight output.
+    """
+    torch = _torch()
+    srcs = list(sources)
+    if not srcs:
+        raise ValueError("need at least one source")
+    B, T, C = (int(x) for x in srcs[0].shape)
+    S = len(srcs)
+    if h is None:
+        h = torch.empty_like(srcs[0])
+    if alpha is True:
+        alpha = torch.empty((B, T, S), dtype=torch.float32, device=srcs[0].device)
+    arr = (c_void_p * S)(*[_ptr(s) for s in srcs])
+    st = lib().hla_attnres_route(_dtype_code(srcs[0]), B, T, C, S, arr, _ptr(w), _ptr(phi_t), float(eps), _ptr(h),
+                                 _ptr(alpha), _stream(stream))
+    _check(st, "hla_attnres_route")
+    return h, alpha

@@ -1,0 +1,177 @@
+"""Host-side tests of the C ABI: symbols, argument validation, workspace sizes,
+RoPE tables. Nothing here launches a kernel or touches a device: every call
+either is pure host code or is rejected by validation before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from softmax_attention_relu_amd import hla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation rejects first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hla.LIB_PATH):
+        from softmax_attention_relu_amd.build import build
+
+        build()
+    return hla.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hla_\w+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 9
+    assert sorted(hla.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(5):
+        assert hla.hla_status_string(code).startswith("HLA_")
+    assert "UNKNOWN" in hla.hla_status_string(99)
+
+
+def test_rope_table_matches_oracle_angles(L):
+    grid, bands = (5, 6, 8), (16, 24, 24)
+    th = oracle.rope3d_angles(oracle.Rope3D(grid, bands, t_offset=3))
+    tt = hla.hla_rope_table_host(5, 3, 16)
+    th_t = th[np.arange(5) * 48, :8]  # tokens (t, 0, 0)
+    np.testing.assert_allclose(tt[..., 0], np.cos(th_t), atol=1e-7)
+    np.testing.assert_allclose(tt[..., 1], np.sin(th_t), atol=1e-7)
+    tw = hla.hla_rope_table_host(8, 0, 24)
+    np.testing.assert_allclose(tw[..., 0], np.cos(th[:8, 20:]), atol=1e-7)
+    np.testing.assert_allclose(tw[..., 1], np.sin(th[:8, 20:]), atol=1e-7)
+    # 720p/60s frame range: angles up to 240 rad still rounded from double
+    big = hla.hla_rope_table_host(241, 0, 16)
+    a = np.arange(241)[:, None] * 10000.0 ** (-2.0 * np.arange(8) / 16)
+    np.testing.assert_allclose(big[..., 1], np.sin(a), atol=1e-7)
+
+
+def test_rope_table_rejects_bad_args(L):
+    out = (ctypes.c_float * 16)()
+    assert L.hla_rope_table_host(0, 0, 16, 1e4, out) == hla.HLA_ERR_INVALID_ARG
+    assert L.hla_rope_table_host(1, 0, 15, 1e4, out) == hla.HLA_ERR_INVALID_ARG
+    assert L.hla_rope_table_host(1, 0, 16, 0.0, out) == hla.HLA_ERR_INVALID_ARG
+    assert L.hla_rope_table_host(1, 0, 16, 1e4, None) == hla.HLA_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(L):
+    w3 = hla.hla_linear_attn_workspace(1, 75600, 32, 64)
+    assert 0 < w3 < 64 << 20  # fp32 partials stay a few percent of the 1.5 GB of tensors
+    assert hla.hla_linear_attn_workspace(1, 75600, 32, 32) == 0
+    assert hla.hla_linear_attn_workspace(0, 10, 1, 64) == 0
+    w5 = hla.hla_linear_attn_chunked_workspace(1, 867600, 32, 64, 36000)
+    assert 0 < w5 < 128 << 20
+    assert hla.hla_linear_attn_chunked_workspace(1, 100, 1, 64, 0) == 0
+    # one chunk covering everything needs the same as the bidirectional call
+    assert hla.hla_linear_attn_chunked_workspace(2, 999, 3, 64, 999) == hla.hla_linear_attn_workspace(2, 999, 3, 64)
+    wa = hla.hla_softmax_anchor_workspace(1, 75600, 32, 64)
+    assert wa == 32 * 64 * 75648 * 2  # V^T padded to 64 tokens
+
+
+def _rope(grid=(2, 2, 2), bands=(16, 24, 24)):
+    s = hla.hla_rope3d()
+    s.grid_t, s.grid_h, s.grid_w = grid
+    s.d_t, s.d_h, s.d_w = bands
+    s.cs_t = s.cs_h = s.cs_w = 0x10000
+    return s
+
+
+def _linear(L, dt=0, B=1, N=8, H=1, D=64, q=FAKE, k=FAKE, v=FAKE, o=FAKE, rope=None, eps=1e-6, ws=FAKE,
+            ws_bytes=1 << 40):
+    return L.hla_linear_attn(dt, B, N, H, D, q, k, v, None, ctypes.byref(rope) if rope else None, eps, o, ws,
+                             ws_bytes, None)
+
+
+def test_linear_validation(L):
+    E = hla
+    assert _linear(L, q=None) == E.HLA_ERR_INVALID_ARG
+    assert _linear(L, o=None) == E.HLA_ERR_INVALID_ARG
+    assert _linear(L, N=0) == E.HLA_ERR_INVALID_ARG
+    assert _linear(L, B=-1) == E.HLA_ERR_INVALID_ARG
+    assert _linear(L, D=128) == E.HLA_ERR_UNSUPPORTED
+    assert _linear(L, dt=7) == E.HLA_ERR_UNSUPPORTED
+    assert _linear(L, eps=-1.0) == E.HLA_ERR_INVALID_ARG
+    assert _linear(L, eps=float("nan")) == E.HLA_ERR_INVALID_ARG
+    assert _linear(L, rope=_rope((2, 2, 3))) == E.HLA_ERR_INVALID_ARG  # grid != N
+    assert _linear(L, rope=_rope((2, 2, 2), (15, 25, 24))) == E.HLA_ERR_INVALID_ARG  # odd band
+    assert _linear(L, rope=_rope((2, 2, 2), (16, 24, 26))) == E.HLA_ERR_INVALID_ARG  # sum != D
+    bad = _rope()
+    bad.cs_h = None
+    assert _linear(L, rope=bad) == E.HLA_ERR_INVALID_ARG
+    assert _linear(L, ws=None) == E.HLA_ERR_WORKSPACE
+    need = hla.hla_linear_attn_workspace(1, 8, 1, 64)
+    assert _linear(L, rope=_rope(), ws_bytes=need - 1) == E.HLA_ERR_WORKSPACE
+
+
+def test_chunked_validation(L):
+    E = hla
+
+    def call(chunk=4, kv_in=None, ks_in=None, kv_out=None, ks_out=None, ws_bytes=1 << 40, ws=FAKE):
+        return L.hla_linear_attn_chunked(0, 1, 8, 1, 64, chunk, FAKE, FAKE, FAKE, None, None, 1e-6, kv_in, ks_in,
+                                         kv_out, ks_out, FAKE, ws, ws_bytes, None)
+
+    assert call(chunk=0) == E.HLA_ERR_INVALID_ARG
+    assert call(chunk=-3) == E.HLA_ERR_INVALID_ARG
+    assert call(kv_in=FAKE) == E.HLA_ERR_INVALID_ARG  # ksum_in missing
+    assert call(ks_out=FAKE) == E.HLA_ERR_INVALID_ARG  # kv_out missing
+    assert call(ws_bytes=16) == E.HLA_ERR_WORKSPACE
+
+
+def test_anchor_validation(L):
+    E = hla
+
+    def call(dt=0, N=8, D=64, scale=0.125, q=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return L.hla_softmax_anchor(dt, 1, N, 1, D, q, FAKE, FAKE, None, scale, FAKE, ws, ws_bytes, None)
+
+    assert call(q=None) == E.HLA_ERR_INVALID_ARG
+    assert call(N=0) == E.HLA_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == E.HLA_ERR_INVALID_ARG
+    assert call(scale=0.0) == E.HLA_ERR_INVALID_ARG
+    assert call(scale=-1.0) == E.HLA_ERR_INVALID_ARG
+    assert call(dt=1) == E.HLA_ERR_UNSUPPORTED
+    assert call(D=32) == E.HLA_ERR_UNSUPPORTED
+    assert call(ws=None) == E.HLA_ERR_WORKSPACE
+    assert call(ws_bytes=64 * 64 * 2 - 1) == E.HLA_ERR_WORKSPACE
+
+
+def test_route_validation(L):
+    E = hla
+
+    def call(S=4, C=2048, srcs=None, w=FAKE, h=FAKE, dt=0, B=1, T=4, eps=1e-6):
+        arr = (ctypes.c_void_p * 16)(*([0x10000] * 16)) if srcs is None else srcs
+        return L.hla_attnres_route(dt, B, T, C, S, arr, w, None, eps, h, None, None)
+
+    assert call(S=0) == E.HLA_ERR_INVALID_ARG
+    assert call(S=17) == E.HLA_ERR_INVALID_ARG
+    assert call(C=12) == E.HLA_ERR_INVALID_ARG
+    assert call(C=0) == E.HLA_ERR_INVALID_ARG
+    assert call(T=0) == E.HLA_ERR_INVALID_ARG
+    assert call(w=None) == E.HLA_ERR_INVALID_ARG
+    assert call(h=None) == E.HLA_ERR_INVALID_ARG
+    assert call(eps=-1.0) == E.HLA_ERR_INVALID_ARG
+    holes = (ctypes.c_void_p * 4)(0x10000, None, 0x10000, 0x10000)
+    assert call(srcs=holes) == E.HLA_ERR_INVALID_ARG
+    assert L.hla_attnres_route(0, 1, 4, 2048, 4, None, FAKE, None, 1e-6, FAKE, None, None) == E.HLA_ERR_INVALID_ARG
+    assert call(C=4104) == E.HLA_ERR_UNSUPPORTED
+    assert call(dt=5) == E.HLA_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(hla, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(hla, "_lib", None)
+    with pytest.raises(ImportError):
+        hla.lib()

@@ -1,0 +1,359 @@
+"""GPU parity: libhla (through its C ABI) against the fp64 oracle.
+
+Inputs come from the seeded generator ``synth``; the oracle decodes the same
+bf16 bits. The error measure is normwise, max|got - ref| / max|ref| over the
+compared outputs (outputs are zero-mean, so an elementwise relative error is
+ill-posed); bars: 1e-2 for bf16 inputs, 1e-5 for float inputs. The oracle is
+called head by head (heads are independent in the definition; a per-head
+einsum is much faster than one over all heads).
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from softmax_attention_relu_amd import hla
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2
+TOL_F32 = 1e-5
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def normwise(got, ref):
+    den = np.abs(ref).max()
+    return float(np.abs(got - ref).max() / den) if den > 0 else float(np.abs(got).max())
+
+
+def tol(dtype):
+    return TOL_BF16 if dtype == "bf16" else TOL_F32
+
+
+def oracle_linear_per_head(x, grid, chunk=0, rows=None, heads=None, bands=(16, 24, 24), t_offset=0, kv_in=None,
+                           ksum_in=None):
+    """Oracle outputs of shape (B, len(rows), len(heads), 64) and the states (B, len(heads), 64, 64), (B, len(heads), 64)."""
+    B, N, H, D = x["q"].shape
+    heads = range(H) if heads is None else heads
+    rope = None if grid is None else oracle.Rope3D(grid, bands, t_offset=t_offset)
+    outs, kvs, kss = [], [], []
+    for h in heads:
+        f = {k: synth.to_f64(v[:, :, h:h + 1]) for k, v in x.items()}
+        g = f.get("g")
+        if chunk:
+            kin = None if kv_in is None else kv_in[:, h:h + 1]
+            sin = None if ksum_in is None else ksum_in[:, h:h + 1]
+            o, kv, ks = oracle.linear_attention_chunked(f["q"], f["k"], f["v"], chunk, g, rope, kv_in=kin,
+                                                        ksum_in=sin, rows=rows)
+        else:
+            o, kv, ks = oracle.linear_attention(f["q"], f["k"], f["v"], g, rope, rows=rows, return_state=True)
+        outs.append(o)
+        kvs.append(kv)
+        kss.append(ks)
+    return np.concatenate(outs, axis=2), np.concatenate(kvs, axis=1), np.concatenate(kss, axis=1)
+
+
+def run_linear(x, grid, chunk=0, bands=(16, 24, 24), t_offset=0, kv_in=None, ksum_in=None, want_state=False,
+               rope_tables=None):
+    d = {k: dev(v) for k, v in x.items()}
+    rope = None
+    if grid is not None:
+        rope = hla.Rope3D(grid, bands, t_offset=t_offset, tables=rope_tables)
+    if chunk:
+        B, N, H, _ = x["q"].shape
+        kin = None if kv_in is None else torch.from_numpy(kv_in.astype(np.float32)).cuda()
+        sin = None if ksum_in is None else torch.from_numpy(ksum_in.astype(np.float32)).cuda()
+        kvo = torch.empty((B, H, 64, 64), dtype=torch.float32, device="cuda") if want_state else None
+        kso = torch.empty((B, H, 64), dtype=torch.float32, device="cuda") if want_state else None
+        o = hla.hla_linear_attn_chunked(d["q"], d["k"], d["v"], chunk, d.get("g"), rope, kv_in=kin, ksum_in=sin,
+                                        kv_out=kvo, ksum_out=kso)
+        torch.cuda.synchronize()
+        if want_state:
+            return o, kvo, kso
+        return o
+    o = hla.hla_linear_attn(d["q"], d["k"], d["v"], d.get("g"), rope)
+    torch.cuda.synchronize()
+    return o
+
+
+# ----------------------------------------------------------------------------
+# linear attention at the measured sizes
+
+@pytest.mark.parametrize("w", [synth.LINEAR_F32_N1024, synth.LINEAR_CFGPAIR_N32760, synth.LINEAR_720P5S],
+                         ids=lambda w: w.name)
+def test_linear_full_size(w):
+    say(f"[parity] {w.name}: B={w.B} N={w.N} H={w.H} dtype={w.dtype} gated={w.gated}")
+    x = w.draw()
+    got = host(run_linear(x, w.grid))
+    ref, _, _ = oracle_linear_per_head(x, w.grid)
+    err = normwise(got, ref)
+    per_head = max(normwise(got[:, :, h], ref[:, :, h]) for h in range(w.H))
+    say(f"[parity] {w.name}: normwise {err:.3e}, worst head {per_head:.3e}")
+    assert err <= tol(w.dtype)
+    assert per_head <= tol(w.dtype)
+
+
+def test_hybrid_linear_layer_sampled_heads():
+    w = synth.HYBRID_LINEAR[0]
+    say(f"[parity] {w.name}")
+    x = w.draw()
+    got = host(run_linear(x, w.grid))
+    heads = [0, 9, 22, 31]
+    ref, _, _ = oracle_linear_per_head(x, w.grid, heads=heads)
+    err = normwise(got[:, :, heads], ref)
+    say(f"[parity] {w.name}: heads {heads} normwise {err:.3e}")
+    assert err <= TOL_BF16
+
+
+def test_chunked_720p60s_sampled():
+    w = synth.CHUNKED_720P60S
+    say(f"[parity] {w.name}: N={w.N} L={w.chunk_tokens} (drawing inputs)")
+    x = w.draw()
+    o, kvo, kso = run_linear(x, w.grid, chunk=w.chunk_tokens, want_state=True)
+    say("[parity] chunked: GPU done")
+    rows = np.unique(np.concatenate([np.arange(0, w.N, 1013), np.arange(35990, 36010), [w.N - 3600, w.N - 1]]))
+    got = host(o[:, torch.from_numpy(rows).cuda()])
+    heads = [0, 17, 31]
+    ref, kv_ref, ks_ref = oracle_linear_per_head(x, w.grid, chunk=w.chunk_tokens, rows=rows, heads=heads)
+    err = normwise(got[:, :, heads], ref)
+    kv_err = normwise(host(kvo)[:, heads], kv_ref)
+    ks_err = normwise(host(kso)[:, heads], ks_ref)
+    say(f"[parity] chunked: out {err:.3e} kv_out {kv_err:.3e} ksum_out {ks_err:.3e}")
+    assert err <= TOL_BF16
+    assert kv_err <= TOL_BF16
+    assert ks_err <= 1e-5
+
+
+# ----------------------------------------------------------------------------
+# small and ragged shapes
+
+GRIDS = {1: (1, 1, 1), 7: (7, 1, 1), 63: (7, 3, 3), 64: (4, 4, 4), 65: (5, 13, 1), 300: (3, 10, 10),
+         1000: (10, 10, 10)}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N", sorted(GRIDS))
+@pytest.mark.parametrize("rope,gated", [(True, True), (False, False), (True, False)])
+def test_linear_small_shapes(dtype, N, rope, gated):
+    B, H = 2, 3
+    shp = (B, N, H, 64)
+    names = ["q", "k", "v"] + (["g"] if gated else [])
+    x = {nm: synth.randn(100 + N, shp, dtype=dtype, stream=i) for i, nm in enumerate(names)}
+    grid = GRIDS[N] if rope else None
+    got = host(run_linear(x, grid))
+    ref, _, _ = oracle_linear_per_head(x, grid)
+    err = normwise(got, ref)
+    assert err <= tol(dtype), err
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N,L", [(300, 64), (300, 100), (300, 1), (1000, 300), (65, 1000), (1000, 17)])
+def test_chunked_small_shapes(dtype, N, L):
+    B, H = 1, 2
+    grid = GRIDS[N]
+    x = {nm: synth.randn(200 + N + L, (B, N, H, 64), dtype=dtype, stream=i) for i, nm in enumerate("qkvg")}
+    kv_in = synth.randn(7, (B, H, 64, 64), dtype="f32").astype(np.float64)
+    ks_in = np.abs(synth.randn(8, (B, H, 64), dtype="f32").astype(np.float64)) * 10
+    o, kvo, kso = run_linear(x, grid, chunk=L, kv_in=kv_in, ksum_in=ks_in, want_state=True)
+    ref, kv_ref, ks_ref = oracle_linear_per_head(x, grid, chunk=L, kv_in=kv_in, ksum_in=ks_in)
+    assert normwise(host(o), ref) <= tol(dtype)
+    assert normwise(host(kvo), kv_ref) <= tol(dtype)
+    assert normwise(host(kso), ks_ref) <= 1e-5
+
+
+def test_chunked_resume_and_aliasing():
+    """Two calls carrying the state (second with t_offset, state updated in place) equal one call."""
+    grid, L = (10, 10, 10), 200
+    x = {nm: synth.randn(301, (1, 1000, 2, 64), stream=i) for i, nm in enumerate("qkv")}
+    full, kv_full, ks_full = run_linear(x, grid, chunk=L, want_state=True)
+    d = {k: dev(v) for k, v in x.items()}
+    kv = torch.zeros((1, 2, 64, 64), dtype=torch.float32, device="cuda")
+    ks = torch.zeros((1, 2, 64), dtype=torch.float32, device="cuda")
+    outs = []
+    for t0, sl in ((0, slice(0, 600)), (6, slice(600, 1000))):
+        frames = (sl.stop - sl.start) // 100
+        rope = hla.Rope3D((frames, 10, 10), t_offset=t0)
+        q, k, v = (d[n][:, sl].contiguous() for n in "qkv")
+        outs.append(hla.hla_linear_attn_chunked(q, k, v, L, None, rope, kv_in=kv, ksum_in=ks, kv_out=kv, ksum_out=ks))
+    torch.cuda.synchronize()
+    split = host(torch.cat(outs, dim=1))
+    ref, kv_ref, ks_ref = oracle_linear_per_head(x, grid, chunk=L)
+    assert normwise(split, ref) <= TOL_BF16
+    assert normwise(host(kv), kv_ref) <= TOL_BF16
+    assert normwise(host(ks), ks_ref) <= 1e-5
+    # same arithmetic on both paths except the partial split: states agree to fp32 rounding
+    assert normwise(host(kv), host(kv_full)) <= 1e-5
+
+
+# ----------------------------------------------------------------------------
+# edge cases and determinism
+
+def test_linear_edge_cases_and_determinism():
+    N, grid = 1000, (10, 10, 10)
+    x = {nm: synth.randn(400, (1, N, 2, 64), stream=i) for i, nm in enumerate("qkv")}
+    q = x["q"].copy()
+    q[0, 5, 1] = synth.randn(401, (64,)) | np.uint16(0x8000)  # all-negative row -> relu(q) = 0
+    x["q"] = q
+    base = run_linear(x, grid)
+    b = host(base)
+    assert np.all(b[0, 5, 1] == 0.0)
+    again = run_linear(x, grid)
+    assert torch.equal(base, again), "repeat call is not bitwise identical"
+    # G = 0 halves the output exactly
+    xg = dict(x, g=np.zeros_like(x["q"]))
+    assert torch.equal(run_linear(xg, grid), base / 2)
+    # zero-angle tables reduce to no RoPE
+    zero = [np.tile(np.array([1.0, 0.0], np.float32), (n, d // 2, 1)) for n, d in zip(grid, (16, 24, 24))]
+    assert torch.equal(run_linear(x, grid, rope_tables=zero), run_linear(x, None))
+
+
+# ----------------------------------------------------------------------------
+# softmax anchor
+
+def run_anchor(x):
+    d = {k: dev(v) for k, v in x.items()}
+    o = hla.hla_softmax_anchor(d["q"], d["k"], d["v"], d.get("g"))
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 300, 1000])
+@pytest.mark.parametrize("gated", [True, False])
+def test_anchor_small_shapes(N, gated):
+    names = ["q", "k", "v"] + (["g"] if gated else [])
+    x = {nm: synth.randn(500 + N, (2, N, 2, 64), stream=i) for i, nm in enumerate(names)}
+    got = host(run_anchor(x))
+    f = {k: synth.to_f64(v) for k, v in x.items()}
+    ref = oracle.softmax_anchor(f["q"], f["k"], f["v"], f.get("g"), scale=0.125)
+    assert normwise(got, ref) <= TOL_BF16
+
+
+def test_anchor_large_logits():
+    """Q scaled by 8: sharp softmax rows, exercises the reference-max refresh."""
+    x = {nm: synth.randn(600, (1, 2000, 2, 64), std=8.0 if nm == "q" else 1.0, stream=i) for i, nm in enumerate("qkv")}
+    got = host(run_anchor(x))
+    f = {k: synth.to_f64(v) for k, v in x.items()}
+    ref = oracle.softmax_anchor(f["q"], f["k"], f["v"], None, scale=0.125)
+    assert normwise(got, ref) <= TOL_BF16
+
+
+def test_anchor_full_size_sampled_rows():
+    w = synth.HYBRID_ANCHOR
+    say(f"[parity] {w.name}: N={w.N} H={w.H}")
+    x = w.draw()
+    o = run_anchor(x)
+    rows = np.unique(np.concatenate([np.linspace(0, w.N - 1, 512).astype(np.int64), [w.N - 1]]))
+    got = host(o[:, torch.from_numpy(rows).cuda()])
+    worst = 0.0
+    for h in range(w.H):
+        f = {k: synth.to_f64(v[:, :, h:h + 1]) for k, v in x.items()}
+        ref = oracle.softmax_anchor(f["q"], f["k"], f["v"], f["g"], scale=w.scale, rows=rows)
+        worst = max(worst, normwise(got[:, :, h:h + 1], ref))
+    say(f"[parity] anchor: worst head normwise {worst:.3e}")
+    assert worst <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------
+# router
+
+def run_route(srcs, w, phi, eps=1e-6, dtype="bf16"):
+    ds = [dev(s) for s in srcs]
+    wd = torch.from_numpy(w).cuda()
+    pd = None if phi is None else torch.from_numpy(phi).cuda()
+    h, a = hla.hla_attnres_route(ds, wd, pd, eps, alpha=True)
+    torch.cuda.synchronize()
+    return h, a
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("S,C", [(1, 64), (2, 8), (4, 2048), (5, 520), (16, 1024), (4, 4096), (3, 1032), (16, 4096)])
+@pytest.mark.parametrize("with_phi", [True, False])
+def test_route_small_shapes(dtype, S, C, with_phi):
+    B, T = 2, 37
+    srcs = [synth.randn(700 + S + C, (B, T, C), dtype=dtype, stream=i) for i in range(S)]
+    w = synth.randn(701, (C,), std=0.02, dtype="f32")
+    phi = synth.randn(702, (B, C), std=0.02, dtype="f32") if with_phi else None
+    h, a = run_route(srcs, w, phi, dtype=dtype)
+    ref_h, ref_a = oracle.attnres_route([synth.to_f64(s) for s in srcs], w.astype(np.float64),
+                                        None if phi is None else phi.astype(np.float64))
+    assert normwise(host(h), ref_h) <= tol(dtype)
+    assert np.abs(host(a) - ref_a).max() <= (1e-5 if dtype == "bf16" else 1e-6)
+
+
+def test_route_large_query_sharp_softmax():
+    srcs = [synth.randn(800, (1, 64, 256), stream=i) for i in range(4)]
+    w = synth.randn(801, (256,), std=3.0, dtype="f32")
+    h, a = run_route(srcs, w, None)
+    ref_h, ref_a = oracle.attnres_route([synth.to_f64(s) for s in srcs], w.astype(np.float64), None)
+    assert normwise(host(h), ref_h) <= TOL_BF16
+    assert np.abs(host(a) - ref_a).max() <= 1e-4
+
+
+def test_route_full_size():
+    wk = synth.HYBRID_ROUTES[0]
+    say(f"[parity] {wk.name}")
+    x = wk.draw()
+    h, a = run_route(x["v"], x["w"], x["phi_t"])
+    ref_h, ref_a = oracle.attnres_route([synth.to_f64(s) for s in x["v"]], x["w"].astype(np.float64),
+                                        x["phi_t"].astype(np.float64))
+    err = normwise(host(h), ref_h)
+    say(f"[parity] route: h normwise {err:.3e}, alpha max abs {np.abs(host(a) - ref_a).max():.3e}")
+    assert err <= TOL_BF16
+    assert np.abs(host(a) - ref_a).max() <= 1e-5
+
+
+# ----------------------------------------------------------------------------
+# golden fixtures (oracle values stored by tests/golden/make_golden.py)
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        doc = json.load(f)
+    return doc, {k: np.asarray(v).reshape(doc["shapes"][k]) for k, v in doc["outputs"].items()}
+
+
+def test_golden_fixtures_on_gpu():
+    doc, outs = _golden("linear_gated_2x2x3.json")
+    inp = doc["inputs"]
+    x = {nm: synth.randn(inp["seed"], inp["shape"], stream=s) for nm, s in inp["streams"].items()}
+    assert normwise(host(run_linear(x, tuple(doc["grid"]))), outs["o"]) <= TOL_BF16
+
+    doc, outs = _golden("chunked_5x2x2_L6.json")
+    inp = doc["inputs"]
+    x = {nm: synth.randn(inp["seed"], inp["shape"], stream=s) for nm, s in inp["streams"].items()}
+    o, kvo, kso = run_linear(x, tuple(doc["grid"]), chunk=doc["chunk_tokens"], want_state=True)
+    assert normwise(host(o), outs["o"]) <= TOL_BF16
+    assert normwise(host(kvo), outs["kv_out"]) <= TOL_BF16
+
+    doc, outs = _golden("anchor_N40.json")
+    inp = doc["inputs"]
+    x = {nm: synth.randn(inp["seed"], inp["shape"], stream=s) for nm, s in inp["streams"].items()}
+    assert normwise(host(run_anchor(x)), outs["o"]) <= TOL_BF16
+
+    doc, outs = _golden("route_B2T3C64S4.json")
+    inp = doc["inputs"]
+    shp = inp["sources"]["shape"]
+    srcs = [synth.randn(inp["seed"], shp, stream=s) for s in inp["sources"]["streams"]]
+    w = synth.randn(inp["seed"], (shp[2],), std=0.02, dtype="f32", stream=100)
+    phi = synth.randn(inp["seed"], (shp[0], shp[2]), std=0.02, dtype="f32", stream=101)
+    h, a = run_route(srcs, w, phi)
+    assert normwise(host(h), outs["h"]) <= TOL_BF16
