@@ -119,6 +119,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="for rocprofv3 counter runs: one untimed step, then a 1 GiB device copy whose "
+                         "counter reading calibrates bytes; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs the path on one GPU; --gpus above 1 is not supported "
@@ -184,6 +187,18 @@ def main() -> int:
                 hla.hla_softmax_anchor(anc["q"], anc["k"], anc["v"], anc["g"], aw.scale, o=anc["o"], ws=anc["ws"])
                 if ev is not None:
                     ev["anchor"][1].record()
+
+    if args.profile_pass:
+        log("[bench] profile pass: one step, then a 1 GiB copy (calibration)")
+        step()
+        torch.cuda.synchronize()
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] profile pass done")
+        return 0
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):

@@ -35,6 +35,8 @@ RopeArgs make_rope(const hla_rope3d *r) {
   ra.cs_t = r->cs_t;
   ra.cs_h = r->cs_h;
   ra.cs_w = r->cs_w;
+  ra.aligned = (r->d_t % 8 == 0) && (r->d_h % 8 == 0) && (r->d_w % 8 == 0) && ((uintptr_t)r->cs_t % 16 == 0) &&
+               ((uintptr_t)r->cs_h % 16 == 0) && ((uintptr_t)r->cs_w % 16 == 0);
   return ra;
 }
 

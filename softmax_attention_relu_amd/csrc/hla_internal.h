@@ -32,6 +32,7 @@ inline FastDiv make_fastdiv(uint32_t d) {
 // t = n / (gh*gw), y = (n % (gh*gw)) / gw, x = n % gw.
 struct RopeArgs {
   int enabled;
+  int aligned;           // band widths multiples of 8 and 16-byte aligned tables
   int d_t, d_h, d_w;
   uint32_t hw, w;        // grid_h * grid_w, grid_w
   FastDiv div_hw, div_w;

@@ -23,9 +23,7 @@ namespace hla {
 
 namespace {
 
-constexpr int kTile = 256;            // tokens per build tile (8 per thread)
-constexpr int kRow16 = kTile + 8;     // bf16 elements per LDS row (16-byte pad)
-constexpr int kRow32 = kTile + 4;     // float elements per LDS row (16-byte pad)
+constexpr int kTile = 256;            // slab granularity: one 64-token tile per wave
 constexpr int kApplySub = 32;         // tokens per wave step in the apply
 
 template <bool kBF16>
@@ -85,24 +83,74 @@ struct BuildArgs {
   float *part;  // [B*H][n_chunks*slabs_per_chunk][kStateFloats]
 };
 
+constexpr int kWTile = 64;           // tokens per wave tile in the build
+constexpr int kWRow16 = kWTile + 8;  // bf16 per LDS row (144 bytes)
+constexpr int kWRow32 = kWTile + 4;  // floats per LDS row (272 bytes)
+constexpr int kWaveLds16 = 2 * kD * kWRow16 * 2;  // C^T and V^T tiles of one wave
+constexpr int kWaveLds32 = 2 * kD * kWRow32 * 4;
+
+// 16-byte granule swizzle of the build's dim-major bf16 tiles. With 144-byte
+// rows, flipping granule bits 1 and 2 by row bits 5 and 4 makes both access
+// patterns hit 16 distinct bank groups per 16 lanes: the transposed stores
+// (rows 8 apart) and the matrix-core operand loads (16 consecutive rows).
+__device__ __forceinline__ int gran_swz(int row) { return (((row >> 5) & 1) << 1) | (((row >> 4) & 1) << 2); }
+
+// cos/sin of the four pairs of one 8-dim chunk. When every band width is a
+// multiple of 8 the chunk lies in one band and the four pairs are contiguous in
+// its table: two aligned 16-byte loads. Otherwise each pair is looked up alone.
+template <bool kAligned>
+struct ChunkRope {
+  RopePair p[kAligned ? 1 : 4];
+  __device__ __forceinline__ void init(const RopeArgs &r, int chunk) {
+#pragma unroll
+    for (int j = 0; j < (kAligned ? 1 : 4); ++j) p[j] = rope_pair(r, 4 * chunk + j);
+  }
+  __device__ __forceinline__ void get(const TokenPos &tp, f32x2_t cs[4]) const {
+    if constexpr (kAligned) {
+      const uint32_t pos = p[0].band == 0 ? tp.t : (p[0].band == 1 ? tp.y : tp.x);
+      const float *q = p[0].col + (size_t)pos * p[0].stride;
+      const f32x4_t a = *reinterpret_cast<const f32x4_t *>(q);
+      const f32x4_t b = *reinterpret_cast<const f32x4_t *>(q + 4);
+      cs[0] = f32x2_t{a.x, a.y};
+      cs[1] = f32x2_t{a.z, a.w};
+      cs[2] = f32x2_t{b.x, b.y};
+      cs[3] = f32x2_t{b.z, b.w};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cs[j] = rope_cs(p[j], tp);
+    }
+  }
+};
+
+// Orders this wave's LDS stores before its later LDS loads (and the reverse)
+// without a work-group barrier: LDS requests of one wave are served in order,
+// the fence keeps the compiler from moving them across.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
-// State build. 256 threads; thread t owns dims 8*(t%8) .. +7 of tokens
-// 8*(t/8) .. +7 of each 256-token tile, so every load instruction of a wave
-// reads eight whole 128-byte token rows. The thread rotates its pairs, then
-// writes its 8x8 block transposed into LDS (dim-major, token-contiguous), the
-// layout the matrix-core operands want: S = C^T V with the token axis as the
-// reduction axis. Wave w accumulates the 32x32 block (w/2, w%2) of S.
-template <bool kBF16>
-__global__ __launch_bounds__(256) void la_build_kernel(BuildArgs a) {
+// State build. Each of the 4 waves of a work-group streams its own 64-token
+// tiles of the slab (tiles w, w+4, ...) with no work-group barrier inside the
+// loop. Lane (dc = lane%8, g = lane/8) loads dims 8*dc..+7 of tokens 8*g..+7:
+// every load instruction reads eight whole 128-byte token rows. The lane
+// applies relu and RoPE, then stores its 8x8 block transposed into the wave's
+// LDS tiles (dim-major, token-contiguous): the layout the matrix cores need,
+// because S = C^T V reduces over tokens. The wave accumulates all of S (four
+// 32x32 blocks) over its tiles; at the end the four waves' partial states are
+// summed in a fixed order through LDS.
+template <bool kBF16, bool kAligned>
+__global__ __launch_bounds__(256, 2) void la_build_kernel(BuildArgs a) {
   typedef Elem<kBF16> E;
   typedef typename E::T T;
   extern __shared__ __align__(16) unsigned char lds_raw[];
 
   const int tid = threadIdx.x;
-  const int dc = tid & 7;   // dim chunk
-  const int g = tid >> 3;   // token group inside the tile
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int dc = lane & 7, g = lane >> 3;
+  const int half = lane >> 5, tl = lane & 31;
 
   const int bh = blockIdx.y;
   const int b = bh / a.H;
@@ -120,21 +168,24 @@ __global__ __launch_bounds__(256) void la_build_kernel(BuildArgs a) {
   const T *kp = reinterpret_cast<const T *>(a.k) + head_base;
   const T *vp = reinterpret_cast<const T *>(a.v) + head_base;
 
-  RopePair rp[4];
-  if (a.rope.enabled) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) rp[j] = rope_pair(a.rope, 4 * dc + j);
-  }
+  ChunkRope<kAligned> cr;
+  if (a.rope.enabled) cr.init(a.rope, dc);
 
   float zacc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
-  f32x16_t acc;
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
 
-  typename E::Chunk kr[8], vr[8];
-  auto load_tile = [&](int base) {
+  unsigned char *wl = lds_raw + wave * (kBF16 ? kWaveLds16 : kWaveLds32);
+
+  for (int base = lo + kWTile * wave; base < hi; base += 4 * kWTile) {
+    typename E::Chunk kr[8], vr[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int n = base + 8 * g + r;
@@ -146,13 +197,10 @@ __global__ __launch_bounds__(256) void la_build_kernel(BuildArgs a) {
         vr[r] = E::zero();
       }
     }
-  };
-
-  if (lo < hi) load_tile(lo);
-  for (int base = lo; base < hi; base += kTile) {
-    __syncthreads();  // previous tile's operand reads are done
-    // relu, key sum, rotation; transposed store into LDS
-    float c[8][8];
+    // relu, key sum, rotation; bf16 tiles pack token pairs right away
+    float c[kBF16 ? 1 : 8][8];
+    uint32_t pk[8][4];
+    float prev[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       float x[8];
@@ -163,25 +211,33 @@ __global__ __launch_bounds__(256) void la_build_kernel(BuildArgs a) {
         zacc[i] += x[i];
       }
       if (a.rope.enabled) {
-        const int n = base + 8 * g + r;
-        const TokenPos tp = token_pos(a.rope, (uint32_t)min(n, a.N - 1));
+        const TokenPos tp = token_pos(a.rope, (uint32_t)min(base + 8 * g + r, a.N - 1));
+        f32x2_t cs[4];
+        cr.get(tp, cs);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], rope_cs(rp[j], tp));
+        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], cs[j]);
       }
+      if constexpr (kBF16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c[r][i] = x[i];
+        for (int i = 0; i < 8; ++i) {
+          if (r & 1)
+            pk[i][r >> 1] = pack_bf16(prev[i], x[i]);
+          else
+            prev[i] = x[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[r][i] = x[i];
+      }
     }
     if constexpr (kBF16) {
-      uint16_t *cT = reinterpret_cast<uint16_t *>(lds_raw);
-      uint16_t *vT = cT + kD * kRow16;
+      uint16_t *cT = reinterpret_cast<uint16_t *>(wl);
+      uint16_t *vT = cT + kD * kWRow16;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        uint4 w;
-        w.x = pack_bf16(c[0][i], c[1][i]);
-        w.y = pack_bf16(c[2][i], c[3][i]);
-        w.z = pack_bf16(c[4][i], c[5][i]);
-        w.w = pack_bf16(c[6][i], c[7][i]);
-        *reinterpret_cast<uint4 *>(cT + (8 * dc + i) * kRow16 + 8 * g) = w;
+        const int row = 8 * dc + i;
+        *reinterpret_cast<uint4 *>(cT + row * kWRow16 + 8 * (g ^ gran_swz(row))) =
+            make_uint4(pk[i][0], pk[i][1], pk[i][2], pk[i][3]);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -189,25 +245,39 @@ __global__ __launch_bounds__(256) void la_build_kernel(BuildArgs a) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const uint4 &q = vr[r].w;
-          const uint32_t word = (i >> 1) == 0 ? q.x : (i >> 1) == 1 ? q.y : (i >> 1) == 2 ? q.z : q.w;
-          wd[r] = word;
+          wd[r] = (i >> 1) == 0 ? q.x : (i >> 1) == 1 ? q.y : (i >> 1) == 2 ? q.z : q.w;
         }
         uint4 w;
         if (i & 1) {
-          w.x = pack_hi16(wd[0], wd[1]); w.y = pack_hi16(wd[2], wd[3]);
-          w.z = pack_hi16(wd[4], wd[5]); w.w = pack_hi16(wd[6], wd[7]);
+          w = make_uint4(pack_hi16(wd[0], wd[1]), pack_hi16(wd[2], wd[3]), pack_hi16(wd[4], wd[5]),
+                         pack_hi16(wd[6], wd[7]));
         } else {
-          w.x = pack_lo16(wd[0], wd[1]); w.y = pack_lo16(wd[2], wd[3]);
-          w.z = pack_lo16(wd[4], wd[5]); w.w = pack_lo16(wd[6], wd[7]);
+          w = make_uint4(pack_lo16(wd[0], wd[1]), pack_lo16(wd[2], wd[3]), pack_lo16(wd[4], wd[5]),
+                         pack_lo16(wd[6], wd[7]));
         }
-        *reinterpret_cast<uint4 *>(vT + (8 * dc + i) * kRow16 + 8 * g) = w;
+        const int row = 8 * dc + i;
+        *reinterpret_cast<uint4 *>(vT + row * kWRow16 + 8 * (g ^ gran_swz(row))) = w;
+      }
+      wave_lds_fence();
+      const int r0 = tl, r1 = 32 + tl;
+#pragma unroll
+      for (int kk = 0; kk < kWTile / 16; ++kk) {
+        const int G = 2 * kk + half;
+        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t *>(cT + r0 * kWRow16 + 8 * (G ^ gran_swz(r0)));
+        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t *>(cT + r1 * kWRow16 + 8 * (G ^ gran_swz(r1)));
+        const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t *>(vT + r0 * kWRow16 + 8 * (G ^ gran_swz(r0)));
+        const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t *>(vT + r1 * kWRow16 + 8 * (G ^ gran_swz(r1)));
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
       }
     } else {
-      float *cT = reinterpret_cast<float *>(lds_raw);
-      float *vT = cT + kD * kRow32;
+      float *cT = reinterpret_cast<float *>(wl);
+      float *vT = cT + kD * kWRow32;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float *dst = cT + (8 * dc + i) * kRow32 + 8 * g;
+        float *dst = cT + (8 * dc + i) * kWRow32 + 8 * g;
         *reinterpret_cast<float4 *>(dst) = make_float4(c[0][i], c[1][i], c[2][i], c[3][i]);
         *reinterpret_cast<float4 *>(dst + 4) = make_float4(c[4][i], c[5][i], c[6][i], c[7][i]);
       }
@@ -220,52 +290,26 @@ __global__ __launch_bounds__(256) void la_build_kernel(BuildArgs a) {
           E::unpack(vr[r], x);
           vv[r] = x[i];
         }
-        float *dst = vT + (8 * dc + i) * kRow32 + 8 * g;
+        float *dst = vT + (8 * dc + i) * kWRow32 + 8 * g;
         *reinterpret_cast<float4 *>(dst) = make_float4(vv[0], vv[1], vv[2], vv[3]);
         *reinterpret_cast<float4 *>(dst + 4) = make_float4(vv[4], vv[5], vv[6], vv[7]);
       }
-    }
-    __syncthreads();
-    // next tile's loads fly while the matrix cores work on this one
-    if (base + kTile < hi) load_tile(base + kTile);
-
-    const int mb = wave >> 1, nb = wave & 1;
-    if constexpr (kBF16) {
-      const uint16_t *cT = reinterpret_cast<const uint16_t *>(lds_raw);
-      const uint16_t *vT = cT + kD * kRow16;
-      const uint16_t *arow = cT + (32 * mb + (lane & 31)) * kRow16 + 8 * (lane >> 5);
-      const uint16_t *brow = vT + (32 * nb + (lane & 31)) * kRow16 + 8 * (lane >> 5);
-#pragma unroll
-      for (int kk = 0; kk < kTile / 16; ++kk) {
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(arow + 16 * kk);
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(brow + 16 * kk);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
-      }
-    } else {
-      const float *cT = reinterpret_cast<const float *>(lds_raw);
-      const float *vT = cT + kD * kRow32;
-      const float *arow = cT + (32 * mb + (lane & 31)) * kRow32 + (lane >> 5);
-      const float *brow = vT + (32 * nb + (lane & 31)) * kRow32 + (lane >> 5);
-#pragma unroll 8
-      for (int kk = 0; kk < kTile / 2; ++kk) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(arow[2 * kk], brow[2 * kk], acc, 0, 0, 0);
+      wave_lds_fence();
+      const float *a0p = cT + tl * kWRow32 + half, *a1p = cT + (32 + tl) * kWRow32 + half;
+      const float *b0p = vT + tl * kWRow32 + half, *b1p = vT + (32 + tl) * kWRow32 + half;
+#pragma unroll 4
+      for (int kk = 0; kk < kWTile / 2; ++kk) {
+        const float a0 = a0p[2 * kk], a1 = a1p[2 * kk], b0 = b0p[2 * kk], b1 = b1p[2 * kk];
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
       }
     }
+    wave_lds_fence();  // the next tile's stores come after these loads
   }
 
-  // partial record of this slab
-  float *out = a.part + ((size_t)bh * a.n_chunks * a.slabs_per_chunk + slab_id) * kStateFloats;
-  {
-    const int mb = wave >> 1, nb = wave & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * mb + 8 * i + 4 * (lane >> 5) + j;
-        out[d * kD + 32 * nb + (lane & 31)] = acc[4 * i + j];
-      }
-  }
-  // key sum: lanes with equal dc (lane bits 3..5 differ), then the four waves
+  // key sum of the wave: lanes with equal dc differ in lane bits 3..5
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float s = zacc[i];
@@ -274,14 +318,28 @@ __global__ __launch_bounds__(256) void la_build_kernel(BuildArgs a) {
     s += __shfl_xor(s, 32);
     zacc[i] = s;
   }
+  // fixed-order sum of the four waves' partial states through LDS
   __syncthreads();
-  float *zw = reinterpret_cast<float *>(lds_raw);  // [4][64]
+  float *red = reinterpret_cast<float *>(lds_raw);  // [4][64*64]
+  float *redz = red + 4 * kD * kD;                  // [4][64]
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          red[wave * kD * kD + (32 * mb + 8 * i + 4 * half + j) * kD + 32 * nb + tl] = acc[mb][nb][4 * i + j];
   if (lane < 8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) zw[wave * kD + 8 * dc + i] = zacc[i];
+    for (int i = 0; i < 8; ++i) redz[wave * kD + 8 * dc + i] = zacc[i];
   }
   __syncthreads();
-  if (tid < kD) out[kD * kD + tid] = zw[tid] + zw[kD + tid] + zw[2 * kD + tid] + zw[3 * kD + tid];
+  float *out = a.part + ((size_t)bh * a.n_chunks * a.slabs_per_chunk + slab_id) * kStateFloats;
+  for (int idx = tid; idx < kD * kD; idx += 256)
+    out[idx] = red[idx] + red[kD * kD + idx] + red[2 * kD * kD + idx] + red[3 * kD * kD + idx];
+  if (tid < kD) out[kD * kD + tid] = redz[tid] + redz[kD + tid] + redz[2 * kD + tid] + redz[3 * kD + tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -320,10 +378,14 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
 // ---------------------------------------------------------------------------
 // Apply. Each wave handles 32 tokens per step: lane l holds token l%32 and
 // the dims of its half (l/32). The numerator is computed transposed,
-// O^T = P^T A^T, so the state is the matrix-core A operand (held in
-// registers for the whole work-group) and each lane's B operand is a
-// contiguous piece of its own token's q row; the result lands with every lane
-// holding output dims of its own token, where the denominator and gate live.
+// O^T = P^T A^T: the chunk's state P (staged once per work-group in LDS as
+// P^T in bf16 hi + lo parts) is the matrix-core A operand and each lane's B
+// operand is a contiguous piece of its own token's q row; the result lands
+// with every lane holding output dims of its own token, where the denominator
+// and the gate are applied. The rows of P^T are stored permuted (output row
+// m = 8i + 4h + j of a 32x32 product holds dim 16h + 4i + j), so the 16
+// results of a lane are 16 consecutive dims: gate loads and output stores are
+// 16 bytes wide.
 struct ApplyArgs {
   const void *q, *g;
   void *o;
@@ -333,11 +395,18 @@ struct ApplyArgs {
   const float *prefix;
 };
 
+constexpr int kSRow = kD + 8;  // bf16 per LDS row of P^T (144 bytes)
+
 // bf16 outputs: hardware exp and reciprocal (about 1 ulp); exactly 1/2 at 0.
 __device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 __device__ __forceinline__ float sigmoid_exact(float x) { return 1.f / (1.f + expf(-x)); }
 
-__global__ __launch_bounds__(256) void la_apply_bf16_kernel(ApplyArgs a) {
+template <bool kAligned>
+__global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
+  __shared__ __align__(16) uint16_t sth[kD * kSRow];
+  __shared__ __align__(16) uint16_t stl[kD * kSRow];
+  __shared__ __align__(16) float zsh[kD];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, tl = lane & 31;
@@ -351,38 +420,30 @@ __global__ __launch_bounds__(256) void la_apply_bf16_kernel(ApplyArgs a) {
   const int hi = min(c_hi, lo + a.apply_tokens);
   if (lo >= hi) return;
 
+  // stage P^T (hi and lo bf16 parts, [e][d]) and the key sum
   const float *P = a.prefix + ((size_t)bh * a.n_chunks + chunk) * kStateFloats;
-  // A operand: P^T as hi + lo bf16 parts. Lane holds rows e = 32*mb + tl,
-  // reduction index d = 16*s + 8*half + t.
-  bf16x8_t shi[2][4], slo[2][4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint32_t wh[4], wl[4];
-#pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        const float x0 = P[(16 * s + 8 * half + t) * kD + 32 * mb + tl];
-        const float x1 = P[(16 * s + 8 * half + t + 1) * kD + 32 * mb + tl];
-        const uint32_t hw = pack_bf16(x0, x1);
-        wh[t / 2] = hw;
-        wl[t / 2] = pack_bf16(x0 - bf16_lo(hw), x1 - bf16_hi(hw));
-      }
-      shi[mb][s] = __builtin_bit_cast(bf16x8_t, make_uint4(wh[0], wh[1], wh[2], wh[3]));
-      slo[mb][s] = __builtin_bit_cast(bf16x8_t, make_uint4(wl[0], wl[1], wl[2], wl[3]));
-    }
+  for (int idx = tid; idx < kD * kD; idx += 256) {
+    const int d = idx >> 6, e = idx & 63;
+    const int el = e & 31;  // dim 16h + 4i + j of block e/32 goes to row 8i + 4h + j
+    const int m = (e & 32) | (((el >> 2) & 3) << 3) | ((el >> 4) << 2) | (el & 3);
+    const float x = P[idx];
+    const uint32_t w = pack_bf16(x, 0.f);
+    sth[m * kSRow + d] = (uint16_t)(w & 0xffffu);
+    stl[m * kSRow + d] = (uint16_t)(pack_bf16(x - bf16_lo(w), 0.f) & 0xffffu);
+  }
+  if (tid < kD) zsh[tid] = P[kD * kD + tid];
+  __syncthreads();
+
   float zr[4][8];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) zr[s][t] = P[kD * kD + 16 * s + 8 * half + t];
+    for (int t = 0; t < 8; ++t) zr[s][t] = zsh[16 * s + 8 * half + t];
 
-  RopePair rp[4][4];
+  ChunkRope<kAligned> cr[4];
   if (a.rope.enabled) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rp[s][j] = rope_pair(a.rope, 8 * s + 4 * half + j);
+    for (int s = 0; s < 4; ++s) cr[s].init(a.rope, 2 * s + half);
   }
 
   const size_t tok_stride = (size_t)a.H * kD;
@@ -399,13 +460,14 @@ __global__ __launch_bounds__(256) void la_apply_bf16_kernel(ApplyArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       qr[s] = valid ? *reinterpret_cast<const uint4 *>(qp + row + 16 * s + 8 * half) : make_uint4(0, 0, 0, 0);
-    uint2 gr[2][4];
+    uint4 gr[2][2];
     if (gp) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          gr[mb][i] = valid ? *reinterpret_cast<const uint2 *>(gp + row + 32 * mb + 8 * i + 4 * half) : make_uint2(0, 0);
+        for (int u = 0; u < 2; ++u)
+          gr[mb][u] = valid ? *reinterpret_cast<const uint4 *>(gp + row + 32 * mb + 16 * half + 8 * u)
+                            : make_uint4(0, 0, 0, 0);
     }
     TokenPos tp;
     if (a.rope.enabled) tp = token_pos(a.rope, (uint32_t)min(n, a.N - 1));
@@ -424,8 +486,10 @@ __global__ __launch_bounds__(256) void la_apply_bf16_kernel(ApplyArgs a) {
         den += x[t] * zr[s][t];
       }
       if (a.rope.enabled) {
+        f32x2_t cs[4];
+        cr[s].get(tp, cs);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], rope_cs(rp[s][j], tp));
+        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], cs[j]);
       }
       bq[s] = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
                                                       pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])));
@@ -437,8 +501,11 @@ __global__ __launch_bounds__(256) void la_apply_bf16_kernel(ApplyArgs a) {
       for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi[mb][s], bq[s], acc[mb], 0, 0, 0);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo[mb][s], bq[s], acc[mb], 0, 0, 0);
+        const int off = (32 * mb + tl) * kSRow + 16 * s + 8 * half;
+        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(sth + off);
+        const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(stl + off);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bq[s], acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bq[s], acc[mb], 0, 0, 0);
       }
     }
     den += __shfl_xor(den, 32);
@@ -447,18 +514,23 @@ __global__ __launch_bounds__(256) void la_apply_bf16_kernel(ApplyArgs a) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float y[4];
+        for (int u = 0; u < 2; ++u) {
+          float y[8];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = acc[mb][4 * i + j] * inv;
+          for (int j = 0; j < 8; ++j) y[j] = acc[mb][8 * u + j] * inv;
           if (gp) {
-            y[0] *= sigmoid_fast(bf16_lo(gr[mb][i].x));
-            y[1] *= sigmoid_fast(bf16_hi(gr[mb][i].x));
-            y[2] *= sigmoid_fast(bf16_lo(gr[mb][i].y));
-            y[3] *= sigmoid_fast(bf16_hi(gr[mb][i].y));
+            const uint4 gw = gr[mb][u];
+            y[0] *= sigmoid_fast(bf16_lo(gw.x));
+            y[1] *= sigmoid_fast(bf16_hi(gw.x));
+            y[2] *= sigmoid_fast(bf16_lo(gw.y));
+            y[3] *= sigmoid_fast(bf16_hi(gw.y));
+            y[4] *= sigmoid_fast(bf16_lo(gw.z));
+            y[5] *= sigmoid_fast(bf16_hi(gw.z));
+            y[6] *= sigmoid_fast(bf16_lo(gw.w));
+            y[7] *= sigmoid_fast(bf16_hi(gw.w));
           }
-          *reinterpret_cast<uint2 *>(op + row + 32 * mb + 8 * i + 4 * half) =
-              make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
+          *reinterpret_cast<uint4 *>(op + row + 32 * mb + 16 * half + 8 * u) =
+              make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7]));
         }
     }
   }
@@ -553,6 +625,16 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+template <bool kBF16, bool kAligned>
+hipError_t launch_build(dim3 grid, const BuildArgs &ba, hipStream_t stream) {
+  const size_t lds = 4 * (size_t)(kBF16 ? kWaveLds16 : kWaveLds32);
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&la_build_kernel<kBF16, kAligned>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((la_build_kernel<kBF16, kAligned>), grid, dim3(256), lds, stream, ba);
+  return hipSuccess;
+}
+
 }  // namespace
 
 LinearPlan plan_linear(int B, int N, int H, int chunk_tokens) {
@@ -602,18 +684,13 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
   ba.rope = a.rope;
   ba.part = part;
   const dim3 bgrid(p.n_chunks * p.slabs_per_chunk, heads);
+  const bool al = a.rope.aligned != 0;
   if (dt == HLA_BF16) {
-    const size_t lds = 2 * kD * kRow16 * sizeof(uint16_t);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&la_build_kernel<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = al ? launch_build<true, true>(bgrid, ba, stream) : launch_build<true, false>(bgrid, ba, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(la_build_kernel<true>, bgrid, dim3(256), lds, stream, ba);
   } else {
-    const size_t lds = 2 * kD * kRow32 * sizeof(float);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&la_build_kernel<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = al ? launch_build<false, true>(bgrid, ba, stream) : launch_build<false, false>(bgrid, ba, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(la_build_kernel<false>, bgrid, dim3(256), lds, stream, ba);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -645,8 +722,10 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
   aa.eps = a.eps;
   aa.prefix = prefix;
   const dim3 agrid(p.n_chunks * p.apply_per_chunk, heads);
-  if (dt == HLA_BF16)
-    hipLaunchKernelGGL(la_apply_bf16_kernel, agrid, dim3(256), 0, stream, aa);
+  if (dt == HLA_BF16 && al)
+    hipLaunchKernelGGL(la_apply_bf16_kernel<true>, agrid, dim3(256), 0, stream, aa);
+  else if (dt == HLA_BF16)
+    hipLaunchKernelGGL(la_apply_bf16_kernel<false>, agrid, dim3(256), 0, stream, aa);
   else
     hipLaunchKernelGGL(la_apply_f32_kernel, agrid, dim3(256), 0, stream, aa);
   return hipGetLastError();
