@@ -141,8 +141,8 @@ __device__ __forceinline__ void wave_lds_fence() {
 // because S = C^T V reduces over tokens. The wave accumulates all of S (four
 // 32x32 blocks) over its tiles; at the end the four waves' partial states are
 // summed in a fixed order through LDS.
-template <bool kBF16, bool kAligned>
-__global__ __launch_bounds__(256, 2) void la_build_kernel(BuildArgs a) {
+template <bool kBF16, bool kRope, bool kAligned>
+__global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs a) {
   typedef Elem<kBF16> E;
   typedef typename E::T T;
   extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void la_build_kernel(BuildArgs a) {
   const T *vp = reinterpret_cast<const T *>(a.v) + head_base;
 
   ChunkRope<kAligned> cr;
-  if (a.rope.enabled) cr.init(a.rope, dc);
+  if constexpr (kRope) cr.init(a.rope, dc);
 
   float zacc[8];
 #pragma unroll
@@ -185,17 +185,19 @@ __global__ __launch_bounds__(256, 2) void la_build_kernel(BuildArgs a) {
   unsigned char *wl = lds_raw + wave * (kBF16 ? kWaveLds16 : kWaveLds32);
 
   for (int base = lo + kWTile * wave; base < hi; base += 4 * kWTile) {
+    // Every load of the tile is issued before any use: token indices past the
+    // slab are clamped to its last token (always valid) and zeroed afterwards.
     typename E::Chunk kr[8], vr[8];
+    f32x2_t cs[kRope ? 8 : 1][4];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int n = base + 8 * g + r;
-      if (n < hi) {
-        kr[r] = E::load(kp + (size_t)n * tok_stride);
-        vr[r] = E::load(vp + (size_t)n * tok_stride);
-      } else {
-        kr[r] = E::zero();
-        vr[r] = E::zero();
-      }
+      const int n = min(base + 8 * g + r, hi - 1);
+      kr[r] = E::load(kp + (size_t)n * tok_stride);
+      vr[r] = E::load(vp + (size_t)n * tok_stride);
+    }
+    if constexpr (kRope) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) cr.get(token_pos(a.rope, (uint32_t)min(base + 8 * g + r, hi - 1)), cs[r]);
     }
     // relu, key sum, rotation; bf16 tiles pack token pairs right away
     float c[kBF16 ? 1 : 8][8];
@@ -203,6 +205,11 @@ __global__ __launch_bounds__(256, 2) void la_build_kernel(BuildArgs a) {
     float prev[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
+      const bool valid = base + 8 * g + r < hi;
+      if (!valid) {
+        kr[r] = E::zero();
+        vr[r] = E::zero();
+      }
       float x[8];
       E::unpack(kr[r], x);
 #pragma unroll
@@ -210,12 +217,9 @@ __global__ __launch_bounds__(256, 2) void la_build_kernel(BuildArgs a) {
         x[i] = fmaxf(x[i], 0.f);
         zacc[i] += x[i];
       }
-      if (a.rope.enabled) {
-        const TokenPos tp = token_pos(a.rope, (uint32_t)min(base + 8 * g + r, a.N - 1));
-        f32x2_t cs[4];
-        cr.get(tp, cs);
+      if constexpr (kRope) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], cs[j]);
+        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], cs[r][j]);
       }
       if constexpr (kBF16) {
 #pragma unroll
@@ -401,7 +405,7 @@ constexpr int kSRow = kD + 8;  // bf16 per LDS row of P^T (144 bytes)
 __device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 __device__ __forceinline__ float sigmoid_exact(float x) { return 1.f / (1.f + expf(-x)); }
 
-template <bool kAligned>
+template <bool kRope, bool kAligned, bool kGate>
 __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
   __shared__ __align__(16) uint16_t sth[kD * kSRow];
   __shared__ __align__(16) uint16_t stl[kD * kSRow];
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
     for (int t = 0; t < 8; ++t) zr[s][t] = zsh[16 * s + 8 * half + t];
 
   ChunkRope<kAligned> cr[4];
-  if (a.rope.enabled) {
+  if constexpr (kRope) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) cr[s].init(a.rope, 2 * s + half);
   }
@@ -449,28 +453,31 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
   const size_t tok_stride = (size_t)a.H * kD;
   const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD;
   const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + head_base;
-  const uint16_t *gp = a.g ? reinterpret_cast<const uint16_t *>(a.g) + head_base : nullptr;
+  const uint16_t *gp = reinterpret_cast<const uint16_t *>(a.g) + head_base;
   uint16_t *op = reinterpret_cast<uint16_t *>(a.o) + head_base;
 
   for (int sub = lo + kApplySub * wave; sub < hi; sub += 4 * kApplySub) {
+    // all loads of the step first; past-the-end tokens read the last valid
+    // token and are neither used for anything visible nor stored
     const int n = sub + tl;
     const bool valid = n < hi;
-    const size_t row = (size_t)n * tok_stride;
+    const size_t row = (size_t)min(n, hi - 1) * tok_stride;
     uint4 qr[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qr[s] = valid ? *reinterpret_cast<const uint4 *>(qp + row + 16 * s + 8 * half) : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < 4; ++s) qr[s] = *reinterpret_cast<const uint4 *>(qp + row + 16 * s + 8 * half);
     uint4 gr[2][2];
-    if (gp) {
+    if constexpr (kGate) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          gr[mb][u] = valid ? *reinterpret_cast<const uint4 *>(gp + row + 32 * mb + 16 * half + 8 * u)
-                            : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < 2; ++u) gr[mb][u] = *reinterpret_cast<const uint4 *>(gp + row + 32 * mb + 16 * half + 8 * u);
     }
-    TokenPos tp;
-    if (a.rope.enabled) tp = token_pos(a.rope, (uint32_t)min(n, a.N - 1));
+    f32x2_t cs[kRope ? 4 : 1][4];
+    if constexpr (kRope) {
+      const TokenPos tp = token_pos(a.rope, (uint32_t)min(n, hi - 1));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) cr[s].get(tp, cs[s]);
+    }
     float den = 0.f;
     bf16x8_t bq[4];
 #pragma unroll
@@ -485,11 +492,9 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
         x[t] = fmaxf(x[t], 0.f);
         den += x[t] * zr[s][t];
       }
-      if (a.rope.enabled) {
-        f32x2_t cs[4];
-        cr[s].get(tp, cs);
+      if constexpr (kRope) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], cs[j]);
+        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], cs[s][j]);
       }
       bq[s] = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
                                                       pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])));
@@ -518,7 +523,7 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
           float y[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) y[j] = acc[mb][8 * u + j] * inv;
-          if (gp) {
+          if constexpr (kGate) {
             const uint4 gw = gr[mb][u];
             y[0] *= sigmoid_fast(bf16_lo(gw.x));
             y[1] *= sigmoid_fast(bf16_hi(gw.x));
@@ -625,14 +630,29 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-template <bool kBF16, bool kAligned>
+template <bool kBF16, bool kRope, bool kAligned>
 hipError_t launch_build(dim3 grid, const BuildArgs &ba, hipStream_t stream) {
   const size_t lds = 4 * (size_t)(kBF16 ? kWaveLds16 : kWaveLds32);
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&la_build_kernel<kBF16, kAligned>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const void *fn = reinterpret_cast<const void *>(&la_build_kernel<kBF16, kRope, kAligned>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((la_build_kernel<kBF16, kAligned>), grid, dim3(256), lds, stream, ba);
+  hipLaunchKernelGGL((la_build_kernel<kBF16, kRope, kAligned>), grid, dim3(256), lds, stream, ba);
   return hipSuccess;
+}
+
+template <bool kBF16>
+hipError_t launch_build_any(const RopeArgs &r, dim3 grid, const BuildArgs &ba, hipStream_t stream) {
+  if (!r.enabled) return launch_build<kBF16, false, false>(grid, ba, stream);
+  if (r.aligned) return launch_build<kBF16, true, true>(grid, ba, stream);
+  return launch_build<kBF16, true, false>(grid, ba, stream);
+}
+
+template <bool kRope, bool kAligned>
+void launch_apply_bf16(bool gate, dim3 grid, const ApplyArgs &aa, hipStream_t stream) {
+  if (gate)
+    hipLaunchKernelGGL((la_apply_bf16_kernel<kRope, kAligned, true>), grid, dim3(256), 0, stream, aa);
+  else
+    hipLaunchKernelGGL((la_apply_bf16_kernel<kRope, kAligned, false>), grid, dim3(256), 0, stream, aa);
 }
 
 }  // namespace
@@ -684,12 +704,9 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
   ba.rope = a.rope;
   ba.part = part;
   const dim3 bgrid(p.n_chunks * p.slabs_per_chunk, heads);
-  const bool al = a.rope.aligned != 0;
-  if (dt == HLA_BF16) {
-    const hipError_t e = al ? launch_build<true, true>(bgrid, ba, stream) : launch_build<true, false>(bgrid, ba, stream);
-    if (e != hipSuccess) return e;
-  } else {
-    const hipError_t e = al ? launch_build<false, true>(bgrid, ba, stream) : launch_build<false, false>(bgrid, ba, stream);
+  {
+    const hipError_t e = dt == HLA_BF16 ? launch_build_any<true>(a.rope, bgrid, ba, stream)
+                                        : launch_build_any<false>(a.rope, bgrid, ba, stream);
     if (e != hipSuccess) return e;
   }
   hipError_t e = hipGetLastError();
@@ -722,11 +739,15 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
   aa.eps = a.eps;
   aa.prefix = prefix;
   const dim3 agrid(p.n_chunks * p.apply_per_chunk, heads);
-  if (dt == HLA_BF16 && al)
-    hipLaunchKernelGGL(la_apply_bf16_kernel<true>, agrid, dim3(256), 0, stream, aa);
-  else if (dt == HLA_BF16)
-    hipLaunchKernelGGL(la_apply_bf16_kernel<false>, agrid, dim3(256), 0, stream, aa);
-  else
+  if (dt == HLA_BF16) {
+    const bool gate = a.g != nullptr;
+    if (!a.rope.enabled)
+      launch_apply_bf16<false, false>(gate, agrid, aa, stream);
+    else if (a.rope.aligned)
+      launch_apply_bf16<true, true>(gate, agrid, aa, stream);
+    else
+      launch_apply_bf16<true, false>(gate, agrid, aa, stream);
+  } else
     hipLaunchKernelGGL(la_apply_f32_kernel, agrid, dim3(256), 0, stream, aa);
   return hipGetLastError();
 }
