@@ -3,7 +3,7 @@
 // section 3.4 causal equation, constant-memory cache and Algorithm 1).
 //
 // One call runs three kernels on the caller's stream:
-//   la_build  per (b, h, slab of tokens): c_j = RoPE(relu(k_j)) and
+//   la_build  per (b, 4 heads, slab of tokens): c_j = RoPE(relu(k_j)) and
 //             S_slab = sum_j c_j^T v_j on the matrix cores (bf16 operands,
 //             fp32 accumulation; fp32 operands for float inputs), plus
 //             z_slab = sum_j relu(k_j) on the vector ALUs. Slabs never straddle
@@ -12,18 +12,21 @@
 //             and an inclusive prefix over chunks, starting from the carried
 //             state; writes one (KV, ksum) record per chunk and the final
 //             state. A bidirectional call is the one-chunk case.
-//   la_apply  per (b, h, token range inside one chunk): a_i = RoPE(relu(q_i)),
-//             numerator a_i P_c on the matrix cores, denominator relu(q_i).Z_c
-//             + eps, optional sigmoid gate, store.
-// Memory traffic is the K/V read of the build and the Q/G read and O write of
-// the apply; the fp32 partials are ~1-2% on top.
+//   la_apply  per (b, 4 heads, token range inside one chunk):
+//             a_i = RoPE(relu(q_i)), numerator a_i P_c on the matrix cores,
+//             denominator relu(q_i).Z_c + eps, optional sigmoid gate, store.
+// Work-groups are 4 waves, one head each, over the same tokens: the 4 waves'
+// 128-byte rows of a token form one 512-byte span of the (B, N, H, 64)
+// tensors, and heads vary fastest across the grid. Memory traffic is the K/V
+// read of the build and the Q/G read and O write of the apply; the fp32
+// partial states are ~2% on top.
 #include "device_common.h"
 
 namespace hla {
 
 namespace {
 
-constexpr int kTile = 256;            // slab granularity: one 64-token tile per wave
+constexpr int kHeadsPerWG = 4;        // one head per wave
 constexpr int kApplySub = 32;         // tokens per wave step in the apply
 
 template <bool kBF16>
@@ -78,7 +81,7 @@ struct Elem<false> {
 
 struct BuildArgs {
   const void *k, *v;
-  int N, H, L, n_chunks, slab_tokens, slabs_per_chunk;
+  int N, H, L, n_chunks, slab_tokens, slabs_per_chunk, ngroups;
   RopeArgs rope;
   float *part;  // [B*H][n_chunks*slabs_per_chunk][kStateFloats]
 };
@@ -132,15 +135,14 @@ __device__ __forceinline__ void wave_lds_fence() {
 }
 
 // ---------------------------------------------------------------------------
-// State build. Each of the 4 waves of a work-group streams its own 64-token
-// tiles of the slab (tiles w, w+4, ...) with no work-group barrier inside the
-// loop. Lane (dc = lane%8, g = lane/8) loads dims 8*dc..+7 of tokens 8*g..+7:
-// every load instruction reads eight whole 128-byte token rows. The lane
-// applies relu and RoPE, then stores its 8x8 block transposed into the wave's
-// LDS tiles (dim-major, token-contiguous): the layout the matrix cores need,
-// because S = C^T V reduces over tokens. The wave accumulates all of S (four
-// 32x32 blocks) over its tiles; at the end the four waves' partial states are
-// summed in a fixed order through LDS.
+// State build. Wave w of a work-group owns head 4*g + w of one slab and streams
+// its 64-token tiles with no work-group barrier. Lane (dc = lane%8,
+// g = lane/8) loads dims 8*dc..+7 of tokens 8*g..+7: every load instruction
+// reads eight whole 128-byte token rows. The lane applies relu and RoPE, then
+// stores its 8x8 block transposed into the wave's LDS tiles (dim-major,
+// token-contiguous), the layout the matrix cores need because S = C^T V
+// reduces over tokens. The wave accumulates all of S (four 32x32 blocks) and
+// writes its slab's partial (S, z) record at the end.
 template <bool kBF16, bool kRope, bool kAligned>
 __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs a) {
   typedef Elem<kBF16> E;
@@ -152,10 +154,12 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
   const int dc = lane & 7, g = lane >> 3;
   const int half = lane >> 5, tl = lane & 31;
 
-  const int bh = blockIdx.y;
-  const int b = bh / a.H;
-  const int h = bh - b * a.H;
-  const int slab_id = blockIdx.x;
+  const int hgroup = blockIdx.x % a.ngroups;
+  const int slab_id = blockIdx.x / a.ngroups;
+  const int h = kHeadsPerWG * hgroup + wave;
+  if (h >= a.H) return;  // no work-group barrier follows
+  const int b = blockIdx.y;
+  const int bh = b * a.H + h;
   const int chunk = slab_id / a.slabs_per_chunk;
   const int slab = slab_id - chunk * a.slabs_per_chunk;
   const int c_lo = chunk * a.L;
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
 
   unsigned char *wl = lds_raw + wave * (kBF16 ? kWaveLds16 : kWaveLds32);
 
-  for (int base = lo + kWTile * wave; base < hi; base += 4 * kWTile) {
+  for (int base = lo; base < hi; base += kWTile) {
     // Every load of the tile is issued before any use: token indices past the
     // slab are clamped to its last token (always valid) and zeroed afterwards.
     typename E::Chunk kr[8], vr[8];
@@ -322,10 +326,7 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
     s += __shfl_xor(s, 32);
     zacc[i] = s;
   }
-  // fixed-order sum of the four waves' partial states through LDS
-  __syncthreads();
-  float *red = reinterpret_cast<float *>(lds_raw);  // [4][64*64]
-  float *redz = red + 4 * kD * kD;                  // [4][64]
+  float *out = a.part + ((size_t)bh * a.n_chunks * a.slabs_per_chunk + slab_id) * kStateFloats;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -333,17 +334,11 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          red[wave * kD * kD + (32 * mb + 8 * i + 4 * half + j) * kD + 32 * nb + tl] = acc[mb][nb][4 * i + j];
+        for (int j = 0; j < 4; ++j) out[(32 * mb + 8 * i + 4 * half + j) * kD + 32 * nb + tl] = acc[mb][nb][4 * i + j];
   if (lane < 8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) redz[wave * kD + 8 * dc + i] = zacc[i];
+    for (int i = 0; i < 8; ++i) out[kD * kD + 8 * dc + i] = zacc[i];
   }
-  __syncthreads();
-  float *out = a.part + ((size_t)bh * a.n_chunks * a.slabs_per_chunk + slab_id) * kStateFloats;
-  for (int idx = tid; idx < kD * kD; idx += 256)
-    out[idx] = red[idx] + red[kD * kD + idx] + red[2 * kD * kD + idx] + red[3 * kD * kD + idx];
-  if (tid < kD) out[kD * kD + tid] = redz[tid] + redz[kD + tid] + redz[2 * kD + tid] + redz[3 * kD + tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -379,70 +374,89 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Apply. Each wave handles 32 tokens per step: lane l holds token l%32 and
-// the dims of its half (l/32). The numerator is computed transposed,
-// O^T = P^T A^T: the chunk's state P (staged once per work-group in LDS as
-// P^T in bf16 hi + lo parts) is the matrix-core A operand and each lane's B
-// operand is a contiguous piece of its own token's q row; the result lands
-// with every lane holding output dims of its own token, where the denominator
-// and the gate are applied. The rows of P^T are stored permuted (output row
-// m = 8i + 4h + j of a 32x32 product holds dim 16h + 4i + j), so the 16
-// results of a lane are 16 consecutive dims: gate loads and output stores are
-// 16 bytes wide.
 struct ApplyArgs {
   const void *q, *g;
   void *o;
-  int N, H, L, n_chunks, apply_tokens, apply_per_chunk;
+  int N, H, L, n_chunks, apply_tokens, apply_per_chunk, ngroups;
   RopeArgs rope;
   float eps;
   const float *prefix;
 };
 
-constexpr int kSRow = kD + 8;  // bf16 per LDS row of P^T (144 bytes)
-
 // bf16 outputs: hardware exp and reciprocal (about 1 ulp); exactly 1/2 at 0.
 __device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 __device__ __forceinline__ float sigmoid_exact(float x) { return 1.f / (1.f + expf(-x)); }
 
+// ---------------------------------------------------------------------------
+// Apply. Wave w of a work-group owns head 4*g + w of one token range inside a
+// chunk and walks it 32 tokens at a time. Q and G are loaded as whole 128-byte
+// rows (lane = token 8u + lane/8, dims 8*(lane%8)..+7) and turned into the
+// matrix-core lane layout through a per-wave LDS stage; O goes back through
+// the stage to whole-row non-temporal stores.
+// In the lane layout, lane l holds token l%32 and the dims of its half (l/32).
+// The numerator is computed transposed, O^T = P^T A^T: the chunk's state P^T
+// (bf16 hi + lo parts, held in registers) is the A operand and each lane's B
+// operand is a contiguous piece of its own token's q row; the result lands
+// with every lane holding output dims of its own token, where the denominator
+// and the gate are applied. The rows of P^T are permuted (output row
+// m = 8i + 4h + j of a 32x32 product holds dim 16h + 4i + j), so the 16
+// results of a lane are 16 consecutive dims.
+constexpr int kStageRow = kD + 8;  // bf16 per staged token row (144 bytes)
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_nt(uint16_t *p, uint4 v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(p));
+}
+
 template <bool kRope, bool kAligned, bool kGate>
 __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
-  __shared__ __align__(16) uint16_t sth[kD * kSRow];
-  __shared__ __align__(16) uint16_t stl[kD * kSRow];
-  __shared__ __align__(16) float zsh[kD];
+  __shared__ __align__(16) uint16_t stage_all[kHeadsPerWG][kApplySub * kStageRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, tl = lane & 31;
-  const int bh = blockIdx.y;
-  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int chunk = blockIdx.x / a.apply_per_chunk;
-  const int part = blockIdx.x - chunk * a.apply_per_chunk;
+  const int r8 = lane >> 3, c8 = lane & 7;
+  const int hgroup = blockIdx.x % a.ngroups;
+  const int pid = blockIdx.x / a.ngroups;
+  const int h = kHeadsPerWG * hgroup + wave;
+  if (h >= a.H) return;  // no work-group barrier follows
+  const int b = blockIdx.y;
+  const int bh = b * a.H + h;
+  const int chunk = pid / a.apply_per_chunk;
+  const int part = pid - chunk * a.apply_per_chunk;
   const int c_lo = chunk * a.L;
   const int c_hi = min(a.N, c_lo + a.L);
   const int lo = c_lo + part * a.apply_tokens;
   const int hi = min(c_hi, lo + a.apply_tokens);
   if (lo >= hi) return;
 
-  // stage P^T (hi and lo bf16 parts, [e][d]) and the key sum
+  // A operand: P^T as hi + lo bf16 parts. Lane holds output row tl of block
+  // mb (dim 32*mb + el) and reduction index d = 16*s + 8*half + t.
   const float *P = a.prefix + ((size_t)bh * a.n_chunks + chunk) * kStateFloats;
-  for (int idx = tid; idx < kD * kD; idx += 256) {
-    const int d = idx >> 6, e = idx & 63;
-    const int el = e & 31;  // dim 16h + 4i + j of block e/32 goes to row 8i + 4h + j
-    const int m = (e & 32) | (((el >> 2) & 3) << 3) | ((el >> 4) << 2) | (el & 3);
-    const float x = P[idx];
-    const uint32_t w = pack_bf16(x, 0.f);
-    sth[m * kSRow + d] = (uint16_t)(w & 0xffffu);
-    stl[m * kSRow + d] = (uint16_t)(pack_bf16(x - bf16_lo(w), 0.f) & 0xffffu);
-  }
-  if (tid < kD) zsh[tid] = P[kD * kD + tid];
-  __syncthreads();
-
+  const int el = (((tl >> 2) & 1) << 4) | ((tl >> 3) << 2) | (tl & 3);
+  bf16x8_t shi[2][4], slo[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        const float x0 = P[(16 * s + 8 * half + t) * kD + 32 * mb + el];
+        const float x1 = P[(16 * s + 8 * half + t + 1) * kD + 32 * mb + el];
+        const uint32_t hw = pack_bf16(x0, x1);
+        wh[t / 2] = hw;
+        wl[t / 2] = pack_bf16(x0 - bf16_lo(hw), x1 - bf16_hi(hw));
+      }
+      shi[mb][s] = __builtin_bit_cast(bf16x8_t, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+      slo[mb][s] = __builtin_bit_cast(bf16x8_t, make_uint4(wl[0], wl[1], wl[2], wl[3]));
+    }
   float zr[4][8];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) zr[s][t] = zsh[16 * s + 8 * half + t];
+    for (int t = 0; t < 8; ++t) zr[s][t] = P[kD * kD + 16 * s + 8 * half + t];
 
   ChunkRope<kAligned> cr[4];
   if constexpr (kRope) {
@@ -452,32 +466,46 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
 
   const size_t tok_stride = (size_t)a.H * kD;
   const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD;
-  const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + head_base;
-  const uint16_t *gp = reinterpret_cast<const uint16_t *>(a.g) + head_base;
-  uint16_t *op = reinterpret_cast<uint16_t *>(a.o) + head_base;
+  const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + head_base + 8 * c8;
+  const uint16_t *gp = reinterpret_cast<const uint16_t *>(a.g) + head_base + 8 * c8;
+  uint16_t *op = reinterpret_cast<uint16_t *>(a.o) + head_base + 8 * c8;
+  uint16_t *st = stage_all[wave];
 
-  for (int sub = lo + kApplySub * wave; sub < hi; sub += 4 * kApplySub) {
-    // all loads of the step first; past-the-end tokens read the last valid
-    // token and are neither used for anything visible nor stored
-    const int n = sub + tl;
-    const bool valid = n < hi;
-    const size_t row = (size_t)min(n, hi - 1) * tok_stride;
-    uint4 qr[4];
+  for (int sub = lo; sub < hi; sub += kApplySub) {
+    // whole-row loads; tokens past the range read the last valid token
+    uint4 qrow[4], grow[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qr[s] = *reinterpret_cast<const uint4 *>(qp + row + 16 * s + 8 * half);
-    uint4 gr[2][2];
-    if constexpr (kGate) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) gr[mb][u] = *reinterpret_cast<const uint4 *>(gp + row + 32 * mb + 16 * half + 8 * u);
+    for (int u = 0; u < 4; ++u) {
+      const size_t n = (size_t)min(sub + 8 * u + r8, hi - 1);
+      qrow[u] = *reinterpret_cast<const uint4 *>(qp + n * tok_stride);
+      if constexpr (kGate) grow[u] = *reinterpret_cast<const uint4 *>(gp + n * tok_stride);
     }
     f32x2_t cs[kRope ? 4 : 1][4];
     if constexpr (kRope) {
-      const TokenPos tp = token_pos(a.rope, (uint32_t)min(n, hi - 1));
+      const TokenPos tp = token_pos(a.rope, (uint32_t)min(sub + tl, hi - 1));
 #pragma unroll
       for (int s = 0; s < 4; ++s) cr[s].get(tp, cs[s]);
     }
+    // q rows -> lane layout
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4 *>(st + (8 * u + r8) * kStageRow + 8 * c8) = qrow[u];
+    wave_lds_fence();
+    uint4 qr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qr[s] = *reinterpret_cast<const uint4 *>(st + tl * kStageRow + 16 * s + 8 * half);
+    uint4 gr[2][2];
+    if constexpr (kGate) {
+      wave_lds_fence();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4 *>(st + (8 * u + r8) * kStageRow + 8 * c8) = grow[u];
+      wave_lds_fence();
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+          gr[mb][v] = *reinterpret_cast<const uint4 *>(st + tl * kStageRow + 32 * mb + 16 * half + 8 * v);
+    }
+
     float den = 0.f;
     bf16x8_t bq[4];
 #pragma unroll
@@ -506,38 +534,43 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
       for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int off = (32 * mb + tl) * kSRow + 16 * s + 8 * half;
-        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(sth + off);
-        const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(stl + off);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bq[s], acc[mb], 0, 0, 0);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bq[s], acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi[mb][s], bq[s], acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo[mb][s], bq[s], acc[mb], 0, 0, 0);
       }
     }
     den += __shfl_xor(den, 32);
     const float inv = 1.f / (den + a.eps);
-    if (valid) {
+    // normalise and gate in the lane layout, back to rows through the stage
+    wave_lds_fence();
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float y[8];
+      for (int v = 0; v < 2; ++v) {
+        float y[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) y[j] = acc[mb][8 * u + j] * inv;
-          if constexpr (kGate) {
-            const uint4 gw = gr[mb][u];
-            y[0] *= sigmoid_fast(bf16_lo(gw.x));
-            y[1] *= sigmoid_fast(bf16_hi(gw.x));
-            y[2] *= sigmoid_fast(bf16_lo(gw.y));
-            y[3] *= sigmoid_fast(bf16_hi(gw.y));
-            y[4] *= sigmoid_fast(bf16_lo(gw.z));
-            y[5] *= sigmoid_fast(bf16_hi(gw.z));
-            y[6] *= sigmoid_fast(bf16_lo(gw.w));
-            y[7] *= sigmoid_fast(bf16_hi(gw.w));
-          }
-          *reinterpret_cast<uint4 *>(op + row + 32 * mb + 16 * half + 8 * u) =
-              make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7]));
+        for (int j = 0; j < 8; ++j) y[j] = acc[mb][8 * v + j] * inv;
+        if constexpr (kGate) {
+          const uint4 gw = gr[mb][v];
+          y[0] *= sigmoid_fast(bf16_lo(gw.x));
+          y[1] *= sigmoid_fast(bf16_hi(gw.x));
+          y[2] *= sigmoid_fast(bf16_lo(gw.y));
+          y[3] *= sigmoid_fast(bf16_hi(gw.y));
+          y[4] *= sigmoid_fast(bf16_lo(gw.z));
+          y[5] *= sigmoid_fast(bf16_hi(gw.z));
+          y[6] *= sigmoid_fast(bf16_lo(gw.w));
+          y[7] *= sigmoid_fast(bf16_hi(gw.w));
         }
+        *reinterpret_cast<uint4 *>(st + tl * kStageRow + 32 * mb + 16 * half + 8 * v) =
+            make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7]));
+      }
+    wave_lds_fence();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n = sub + 8 * u + r8;
+      const uint4 w = *reinterpret_cast<const uint4 *>(st + (8 * u + r8) * kStageRow + 8 * c8);
+      if (n < hi) store_nt(op + (size_t)n * tok_stride, w);
     }
+    wave_lds_fence();  // the next step's stage stores come after these loads
   }
 }
 
@@ -548,10 +581,14 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, tl = lane & 31;
-  const int bh = blockIdx.y;
-  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int chunk = blockIdx.x / a.apply_per_chunk;
-  const int part = blockIdx.x - chunk * a.apply_per_chunk;
+  const int hgroup = blockIdx.x % a.ngroups;
+  const int pid = blockIdx.x / a.ngroups;
+  const int h = kHeadsPerWG * hgroup + wave;
+  if (h >= a.H) return;
+  const int b = blockIdx.y;
+  const int bh = b * a.H + h;
+  const int chunk = pid / a.apply_per_chunk;
+  const int part = pid - chunk * a.apply_per_chunk;
   const int c_lo = chunk * a.L;
   const int c_hi = min(a.N, c_lo + a.L);
   const int lo = c_lo + part * a.apply_tokens;
@@ -574,7 +611,7 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
   const float *gp = a.g ? reinterpret_cast<const float *>(a.g) + head_base : nullptr;
   float *op = reinterpret_cast<float *>(a.o) + head_base;
 
-  for (int sub = lo + kApplySub * wave; sub < hi; sub += 4 * kApplySub) {
+  for (int sub = lo; sub < hi; sub += kApplySub) {
     const int n = sub + tl;
     const bool valid = n < hi;
     const size_t row = (size_t)n * tok_stride;
@@ -662,23 +699,22 @@ LinearPlan plan_linear(int B, int N, int H, int chunk_tokens) {
   const long long L = chunk_tokens > 0 && chunk_tokens < N ? chunk_tokens : N;
   p.chunk_len = (int)L;
   p.n_chunks = (int)((N + L - 1) / L);
-  const long long heads = (long long)B * H;
-  // about 1024 build work-groups (4 per CU), slabs a multiple of the tile
-  long long want = (heads * N + 1023) / 1024;
-  long long slab = ((want + kTile - 1) / kTile) * kTile;
-  if (slab < kTile) slab = kTile;
-  const long long lt = ((L + kTile - 1) / kTile) * kTile;
-  if (slab > lt) slab = lt;
+  p.ngroups = (H + kHeadsPerWG - 1) / kHeadsPerWG;
+  // about 512 work-groups per kernel (two per CU, one round), slabs and apply
+  // ranges whole multiples of the 64-token build tile and 32-token apply step
+  const long long per_chunk_groups = (long long)B * p.ngroups * p.n_chunks;
+  const long long target = 512;
+  long long split = (target + per_chunk_groups - 1) / per_chunk_groups;
+  if (split < 1) split = 1;
+  long long slab = (L + split - 1) / split;
+  slab = ((slab + kWTile - 1) / kWTile) * kWTile;
   p.slab_tokens = (int)slab;
   p.slabs_per_chunk = (int)((L + slab - 1) / slab);
-  // about 2048 apply work-groups, token ranges a multiple of 128
-  long long awant = (heads * N + 2047) / 2048;
-  long long at = ((awant + 127) / 128) * 128;
-  if (at < 128) at = 128;
-  const long long l128 = ((L + 127) / 128) * 128;
-  if (at > l128) at = l128;
+  long long at = (L + split - 1) / split;
+  at = ((at + kApplySub - 1) / kApplySub) * kApplySub;
   p.apply_tokens = (int)at;
   p.apply_per_chunk = (int)((L + at - 1) / at);
+  const long long heads = (long long)B * H;
   const size_t part_bytes = (size_t)heads * p.n_chunks * p.slabs_per_chunk * kStateFloats * sizeof(float);
   const size_t prefix_bytes = (size_t)heads * p.n_chunks * kStateFloats * sizeof(float);
   p.part_offset = 0;
@@ -701,9 +737,10 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
   ba.n_chunks = p.n_chunks;
   ba.slab_tokens = p.slab_tokens;
   ba.slabs_per_chunk = p.slabs_per_chunk;
+  ba.ngroups = p.ngroups;
   ba.rope = a.rope;
   ba.part = part;
-  const dim3 bgrid(p.n_chunks * p.slabs_per_chunk, heads);
+  const dim3 bgrid(p.n_chunks * p.slabs_per_chunk * p.ngroups, a.B);
   {
     const hipError_t e = dt == HLA_BF16 ? launch_build_any<true>(a.rope, bgrid, ba, stream)
                                         : launch_build_any<false>(a.rope, bgrid, ba, stream);
@@ -735,10 +772,11 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
   aa.n_chunks = p.n_chunks;
   aa.apply_tokens = p.apply_tokens;
   aa.apply_per_chunk = p.apply_per_chunk;
+  aa.ngroups = p.ngroups;
   aa.rope = a.rope;
   aa.eps = a.eps;
   aa.prefix = prefix;
-  const dim3 agrid(p.n_chunks * p.apply_per_chunk, heads);
+  const dim3 agrid(p.n_chunks * p.apply_per_chunk * p.ngroups, a.B);
   if (dt == HLA_BF16) {
     const bool gate = a.g != nullptr;
     if (!a.rope.enabled)
