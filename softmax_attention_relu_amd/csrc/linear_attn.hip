@@ -412,8 +412,6 @@ __device__ __forceinline__ void store_nt(uint16_t *p, uint4 v) {
 template <bool kRope, bool kAligned, bool kGate>
 __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
   __shared__ __align__(16) uint16_t stage_all[kHeadsPerWG][kApplySub * kStageRow];
-  __shared__ __align__(16) uint16_t slo_all[kHeadsPerWG][kD * kStageRow];  // P^T lo part, [row][d]
-  __shared__ __align__(16) float z_all[kHeadsPerWG][kD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -434,13 +432,10 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
   if (lo >= hi) return;
 
   // A operand: P^T as hi + lo bf16 parts. Lane holds output row tl of block
-  // mb (dim 32*mb + el) and reduction index d = 16*s + 8*half + t. The hi part
-  // stays in registers, the lo part and the key sum in this wave's LDS.
+  // mb (dim 32*mb + el) and reduction index d = 16*s + 8*half + t.
   const float *P = a.prefix + ((size_t)bh * a.n_chunks + chunk) * kStateFloats;
   const int el = (((tl >> 2) & 1) << 4) | ((tl >> 3) << 2) | (tl & 3);
-  uint16_t *slo_w = slo_all[wave];
-  float *z_w = z_all[wave];
-  bf16x8_t shi[2][4];
+  bf16x8_t shi[2][4], slo[2][4];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -455,10 +450,13 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
         wl[t / 2] = pack_bf16(x0 - bf16_lo(hw), x1 - bf16_hi(hw));
       }
       shi[mb][s] = __builtin_bit_cast(bf16x8_t, make_uint4(wh[0], wh[1], wh[2], wh[3]));
-      *reinterpret_cast<uint4 *>(slo_w + (32 * mb + tl) * kStageRow + 16 * s + 8 * half) =
-          make_uint4(wl[0], wl[1], wl[2], wl[3]);
+      slo[mb][s] = __builtin_bit_cast(bf16x8_t, make_uint4(wl[0], wl[1], wl[2], wl[3]));
     }
-  z_w[lane] = P[kD * kD + lane];
+  float zr[4][8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) zr[s][t] = P[kD * kD + 16 * s + 8 * half + t];
 
   ChunkRope<kAligned> cr[4];
   if constexpr (kRope) {
@@ -473,21 +471,15 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
   uint16_t *op = reinterpret_cast<uint16_t *>(a.o) + head_base + 8 * c8;
   uint16_t *st = stage_all[wave];
 
-  // whole-row loads, one step ahead; tokens past the range read the last
-  // valid token and are never stored
-  uint4 qrow[4], grow[4];
-  auto load_rows = [&](int base) {
+  for (int sub = lo; sub < hi; sub += kApplySub) {
+    // whole-row loads; tokens past the range read the last valid token
+    uint4 qrow[4], grow[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const size_t n = (size_t)min(base + 8 * u + r8, hi - 1);
+      const size_t n = (size_t)min(sub + 8 * u + r8, hi - 1);
       qrow[u] = *reinterpret_cast<const uint4 *>(qp + n * tok_stride);
       if constexpr (kGate) grow[u] = *reinterpret_cast<const uint4 *>(gp + n * tok_stride);
     }
-  };
-  load_rows(lo);
-  wave_lds_fence();
-
-  for (int sub = lo; sub < hi; sub += kApplySub) {
     f32x2_t cs[kRope ? 4 : 1][4];
     if constexpr (kRope) {
       const TokenPos tp = token_pos(a.rope, (uint32_t)min(sub + tl, hi - 1));
@@ -513,7 +505,6 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
         for (int v = 0; v < 2; ++v)
           gr[mb][v] = *reinterpret_cast<const uint4 *>(st + tl * kStageRow + 32 * mb + 16 * half + 8 * v);
     }
-    if (sub + kApplySub < hi) load_rows(sub + kApplySub);
 
     float den = 0.f;
     bf16x8_t bq[4];
@@ -524,13 +515,10 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
       x[2] = bf16_lo(qr[s].y); x[3] = bf16_hi(qr[s].y);
       x[4] = bf16_lo(qr[s].z); x[5] = bf16_hi(qr[s].z);
       x[6] = bf16_lo(qr[s].w); x[7] = bf16_hi(qr[s].w);
-      const f32x4_t z0 = *reinterpret_cast<const f32x4_t *>(z_w + 16 * s + 8 * half);
-      const f32x4_t z1 = *reinterpret_cast<const f32x4_t *>(z_w + 16 * s + 8 * half + 4);
-      const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         x[t] = fmaxf(x[t], 0.f);
-        den += x[t] * zz[t];
+        den += x[t] * zr[s][t];
       }
       if constexpr (kRope) {
 #pragma unroll
@@ -546,10 +534,8 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
       for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8_t sl =
-            *reinterpret_cast<const bf16x8_t *>(slo_w + (32 * mb + tl) * kStageRow + 16 * s + 8 * half);
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi[mb][s], bq[s], acc[mb], 0, 0, 0);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl, bq[s], acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo[mb][s], bq[s], acc[mb], 0, 0, 0);
       }
     }
     den += __shfl_xor(den, 32);
