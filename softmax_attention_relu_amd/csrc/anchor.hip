@@ -87,8 +87,10 @@ struct FwdArgs {
   float c;  // scale * log2(e)
 };
 
-template <int RB>
-__global__ __launch_bounds__(256) void anchor_fwd_kernel(FwdArgs a) {
+template <int RB, int WAVES, int MINW>
+__global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kLoads = kBK * 8 / kThreads;  // 16-byte chunks of K (and of V^T) per thread per tile
   __shared__ __align__(16) uint16_t ks[2][kBK * kKRow];
   __shared__ __align__(16) uint16_t vs[2][kD * kVRow];
 
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void anchor_fwd_kernel(FwdArgs a) {
   const int half = lane >> 5, tl = lane & 31;
   const int bh = blockIdx.y;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int q0 = blockIdx.x * (128 * RB) + wave * (32 * RB);
+  const int q0 = blockIdx.x * (32 * RB * WAVES) + wave * (32 * RB);
 
   const size_t tok_stride = (size_t)a.H * kD;
   const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD;
@@ -117,14 +119,14 @@ __global__ __launch_bounds__(256) void anchor_fwd_kernel(FwdArgs a) {
     }
   }
 
-  // tile loader: 256 threads x 2 chunks of K (64 keys x 8 chunks) and of V^T
-  // (64 dims x 8 chunks)
-  uint4 kreg[2], vreg[2];
+  // tile loader: K (64 keys x 8 chunks) and V^T (64 dims x 8 chunks), 16-byte
+  // chunks spread over the work-group
+  uint4 kreg[kLoads], vreg[kLoads];
   auto load_tile = [&](int t) {
     const int n0 = t * kBK;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int c = tid + 256 * r;
+    for (int r = 0; r < kLoads; ++r) {
+      const int c = tid + kThreads * r;
       const int row = c >> 3, ch = c & 7;
       const int n = n0 + row;
       kreg[r] = n < a.N ? *reinterpret_cast<const uint4 *>(kp + (size_t)n * tok_stride + 8 * ch) : make_uint4(0, 0, 0, 0);
@@ -133,8 +135,8 @@ __global__ __launch_bounds__(256) void anchor_fwd_kernel(FwdArgs a) {
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int c = tid + 256 * r;
+    for (int r = 0; r < kLoads; ++r) {
+      const int c = tid + kThreads * r;
       const int row = c >> 3, ch = c & 7;
       *reinterpret_cast<uint4 *>(&ks[buf][row * kKRow + 8 * ch]) = kreg[r];
       *reinterpret_cast<uint4 *>(&vs[buf][row * kVRow + 8 * ch]) = vreg[r];
@@ -306,7 +308,7 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  constexpr int RB = 2;
+  constexpr int RB = 1, WAVES = 8, MINW = 4;
   FwdArgs fa;
   fa.q = reinterpret_cast<const uint16_t *>(a.q);
   fa.k = reinterpret_cast<const uint16_t *>(a.k);
@@ -317,8 +319,9 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   fa.H = a.H;
   fa.npad = npad;
   fa.c = a.scale * 1.4426950408889634f;
-  const int rows = 128 * RB;
-  hipLaunchKernelGGL(anchor_fwd_kernel<RB>, dim3((a.N + rows - 1) / rows, heads), dim3(256), 0, stream, fa);
+  const int rows = 32 * RB * WAVES;
+  hipLaunchKernelGGL((anchor_fwd_kernel<RB, WAVES, MINW>), dim3((a.N + rows - 1) / rows, heads), dim3(64 * WAVES), 0,
+                     stream, fa);
   return hipGetLastError();
 }
 
