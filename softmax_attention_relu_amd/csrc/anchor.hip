@@ -8,8 +8,8 @@
 //              tokens zero-padded to a multiple of 64 and permuted inside each
 //              group of 16 so that every matrix-core operand of the P.V product
 //              is one contiguous 16-byte LDS read (see kernel comment).
-//   anchor_fwd online-softmax attention. A work-group owns 64*RB*4 query rows
-//              of one (b, h); wave w owns 32*RB rows. Per 64-key tile:
+//   anchor_fwd online-softmax attention. A work-group of 8 waves owns 256
+//              query rows of one (b, h); wave w owns 32 rows. Per 64-key tile:
 //                S^T = K Q^T   (A = K rows from LDS, B = Q^T held in registers)
 //                softmax update in the exp2 domain, lane-local: the score layout
 //                gives each lane one query row and 32 of the 64 keys
@@ -17,6 +17,10 @@
 //                score registers, rounded to bf16)
 //              K and V^T tiles are double-buffered in LDS; the next tile's
 //              global loads are issued before the current tile's products.
+// 128 registers per lane keep every accumulator in VGPRs and let four waves
+// per SIMD interleave their softmax (vector ALU) with their products (matrix
+// cores); the tile's row max is combined across the two lane halves with
+// v_permlane32_swap.
 // The running max is refreshed lazily: rows keep their reference max until a
 // tile exceeds it by more than 8 (log2 units), so exponentials stay <= 2^8
 // and the O / row-sum rescale is almost never taken. The normaliser uses the
@@ -31,10 +35,19 @@ constexpr int kBK = 64;            // keys per tile
 constexpr int kKRow = kD + 8;      // bf16 per LDS row of K (144 bytes)
 constexpr int kVRow = kBK + 8;     // bf16 per LDS row of V^T (144 bytes)
 constexpr float kLazy = 8.0f;      // lazy max threshold, log2 units
+constexpr int kWaves = 8;          // waves per work-group, 32 query rows each
+constexpr int kMinWaves = 4;       // waves per SIMD the forward kernel is compiled for
 
 // Key position inside a group of 16 with bits 2 and 3 swapped. With this
 // order, the 8 keys a lane feeds to one 32x32x16 product (keys 4h..4h+3 and
 // 8+4h..8+4h+3 of a 16-key step, h = lane / 32) sit at positions 8h..8h+7.
+// max of x over lanes l and l^32: v_permlane32_swap of a register with itself
+// leaves the partner's value in one of the two results
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ int perm16(int n) { return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1); }
 
 struct VtArgs {
@@ -90,7 +103,9 @@ struct FwdArgs {
 template <int RB, int WAVES, int MINW>
 __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a) {
   constexpr int kThreads = 64 * WAVES;
-  constexpr int kLoads = kBK * 8 / kThreads;  // 16-byte chunks of K (and of V^T) per thread per tile
+  // 16-byte chunks of K (and of V^T) per thread per tile: 512 chunks each
+  constexpr int kLoaders = kThreads < kBK * 8 ? kThreads : kBK * 8;
+  constexpr int kLoads = kBK * 8 / kLoaders;
   __shared__ __align__(16) uint16_t ks[2][kBK * kKRow];
   __shared__ __align__(16) uint16_t vs[2][kD * kVRow];
 
@@ -126,7 +141,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     const int n0 = t * kBK;
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
-      const int c = tid + kThreads * r;
+      const int c = min(tid, kLoaders - 1) + kLoaders * r;
       const int row = c >> 3, ch = c & 7;
       const int n = n0 + row;
       kreg[r] = n < a.N ? *reinterpret_cast<const uint4 *>(kp + (size_t)n * tok_stride + 8 * ch) : make_uint4(0, 0, 0, 0);
@@ -134,9 +149,10 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     }
   };
   auto store_tile = [&](int buf) {
+    if (tid >= kLoaders) return;
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
-      const int c = tid + kThreads * r;
+      const int c = tid + kLoaders * r;
       const int row = c >> 3, ch = c & 7;
       *reinterpret_cast<uint4 *>(&ks[buf][row * kKRow + 8 * ch]) = kreg[r];
       *reinterpret_cast<uint4 *>(&vs[buf][row * kVRow + 8 * ch]) = vreg[r];
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[rb][kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_halves(mx);
       const float mt = mx * a.c;
       const bool bump = mt > mref[rb] + kLazy;
       if (__any(bump)) {
@@ -308,7 +324,7 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  constexpr int RB = 1, WAVES = 8, MINW = 4;
+  constexpr int RB = 1, WAVES = kWaves, MINW = kMinWaves;
   FwdArgs fa;
   fa.q = reinterpret_cast<const uint16_t *>(a.q);
   fa.k = reinterpret_cast<const uint16_t *>(a.k);
