@@ -189,9 +189,21 @@ def main() -> int:
                     ev["anchor"][1].record()
 
     if args.profile_pass:
-        log("[bench] profile pass: one step, then a 1 GiB copy (calibration)")
+        log("[bench] profile pass: one step, one 720p/60s chunked call, then a 1 GiB copy (calibration)")
         step()
         torch.cuda.synchronize()
+        if not args.no_legs:
+            del lin, routes
+            torch.cuda.empty_cache()
+            cw = synth.CHUNKED_720P60S
+            cx = {k: dev(v) for k, v in cw.draw().items()}
+            ws = torch.empty(hla.hla_linear_attn_chunked_workspace(cw.B, cw.N, cw.H, cw.D, cw.chunk_tokens),
+                             dtype=torch.uint8, device="cuda")
+            hla.hla_linear_attn_chunked(cx["q"], cx["k"], cx["v"], cw.chunk_tokens, None,
+                                        hla.Rope3D(cw.grid, cw.bands, cw.base), cw.eps, ws=ws)
+            torch.cuda.synchronize()
+            del cx, ws
+            torch.cuda.empty_cache()
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
