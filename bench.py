@@ -51,22 +51,24 @@ def _src_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel: str, src_hash: str):
+def _traffic(kernel: str, grid: int, src_hash: str):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None.
 
-    profiles/hbm_traffic.txt holds one line per kernel:
-      kernel=<name> fetch_kib=<F> write_kib=<W> scale=<s> src=<sha>
-    (KiB per dispatch as the counters read them; scale turns counter KiB into
-    bytes, measured on a copy of known size). Lines whose src hash differs from
-    the current kernel source are stale and ignored.
+    profiles/hbm_traffic.txt holds one line per kernel and launch size:
+      kernel=<name> grid=<threads> fetch_kib=<F> write_kib=<W>
+      fetch_scale=<bytes per counter KiB> write_scale=<...> src=<sha>
+    F and W are FETCH_SIZE and WRITE_SIZE per dispatch as the counters read
+    them; the scales turn them into bytes and were measured on a copy of known
+    size. A line whose src hash differs from the current kernel source is stale
+    and ignored, so a changed kernel reports null until it is profiled again.
     """
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     for line in open(path):
         kv = dict(re.findall(r"(\w+)=(\S+)", line))
-        if kv.get("kernel") == kernel and kv.get("src") == src_hash:
-            return (float(kv["fetch_kib"]) + float(kv["write_kib"])) * float(kv["scale"])
+        if kv.get("kernel") == kernel and kv.get("grid") == str(grid) and kv.get("src") == src_hash:
+            return float(kv["fetch_kib"]) * float(kv["fetch_scale"]) + float(kv["write_kib"]) * float(kv["write_scale"])
     return None
 
 
@@ -243,7 +245,9 @@ def main() -> int:
     rt_bytes = rw0.B * rw0.T * rw0.C * 2 * (rw0.S + 1)
     rt_gbs = rt_bytes / (rt_ms * 1e-3) / 1e9
 
-    anchor_traffic = _traffic("anchor_fwd_kernel", _src_hash("anchor.hip"))
+    # anchor_fwd_kernel launches 512 threads per 256 query rows of one head
+    anchor_threads = -(-aw.N // 256) * aw.B * aw.H * 512
+    anchor_traffic = _traffic("anchor_fwd_kernel", anchor_threads, _src_hash("anchor.hip"))
     out = {
         "metric": "linear-attn tokens/s & HBM GB/s at 720p/5s shape; anchor MFMA util %",
         "value": w0.B * w0.N / (lin_ms * 1e-3),

@@ -405,12 +405,12 @@ constexpr int kStageRow = kD + 8;  // bf16 per staged token row (144 bytes)
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void store_nt(uint16_t *p, uint4 v) {
-  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(p));
+__device__ __forceinline__ void store_nt(uint16_t *p, u32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
 }
 
 template <bool kRope, bool kAligned, bool kGate>
-__global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
+__global__ __launch_bounds__(256, (kRope && !kAligned) ? 1 : 2) void la_apply_bf16_kernel(ApplyArgs a) {
   __shared__ __align__(16) uint16_t stage_all[kHeadsPerWG][kApplySub * kStageRow];
 
   const int tid = threadIdx.x;
@@ -473,12 +473,12 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
 
   for (int sub = lo; sub < hi; sub += kApplySub) {
     // whole-row loads; tokens past the range read the last valid token
-    uint4 qrow[4], grow[4];
+    u32x4_t qrow[4], grow[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const size_t n = (size_t)min(sub + 8 * u + r8, hi - 1);
-      qrow[u] = *reinterpret_cast<const uint4 *>(qp + n * tok_stride);
-      if constexpr (kGate) grow[u] = *reinterpret_cast<const uint4 *>(gp + n * tok_stride);
+      qrow[u] = *reinterpret_cast<const u32x4_t *>(qp + n * tok_stride);
+      if constexpr (kGate) grow[u] = *reinterpret_cast<const u32x4_t *>(gp + n * tok_stride);
     }
     f32x2_t cs[kRope ? 4 : 1][4];
     if constexpr (kRope) {
@@ -488,22 +488,22 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
     }
     // q rows -> lane layout
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4 *>(st + (8 * u + r8) * kStageRow + 8 * c8) = qrow[u];
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4_t *>(st + (8 * u + r8) * kStageRow + 8 * c8) = qrow[u];
     wave_lds_fence();
-    uint4 qr[4];
+    u32x4_t qr[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qr[s] = *reinterpret_cast<const uint4 *>(st + tl * kStageRow + 16 * s + 8 * half);
-    uint4 gr[2][2];
+    for (int s = 0; s < 4; ++s) qr[s] = *reinterpret_cast<const u32x4_t *>(st + tl * kStageRow + 16 * s + 8 * half);
+    u32x4_t gr[2][2];
     if constexpr (kGate) {
       wave_lds_fence();
 #pragma unroll
-      for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4 *>(st + (8 * u + r8) * kStageRow + 8 * c8) = grow[u];
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4_t *>(st + (8 * u + r8) * kStageRow + 8 * c8) = grow[u];
       wave_lds_fence();
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int v = 0; v < 2; ++v)
-          gr[mb][v] = *reinterpret_cast<const uint4 *>(st + tl * kStageRow + 32 * mb + 16 * half + 8 * v);
+          gr[mb][v] = *reinterpret_cast<const u32x4_t *>(st + tl * kStageRow + 32 * mb + 16 * half + 8 * v);
     }
 
     float den = 0.f;
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) y[j] = acc[mb][8 * v + j] * inv;
         if constexpr (kGate) {
-          const uint4 gw = gr[mb][v];
+          const u32x4_t gw = gr[mb][v];
           y[0] *= sigmoid_fast(bf16_lo(gw.x));
           y[1] *= sigmoid_fast(bf16_hi(gw.x));
           y[2] *= sigmoid_fast(bf16_lo(gw.y));
@@ -560,14 +560,14 @@ __global__ __launch_bounds__(256, 2) void la_apply_bf16_kernel(ApplyArgs a) {
           y[6] *= sigmoid_fast(bf16_lo(gw.w));
           y[7] *= sigmoid_fast(bf16_hi(gw.w));
         }
-        *reinterpret_cast<uint4 *>(st + tl * kStageRow + 32 * mb + 16 * half + 8 * v) =
-            make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7]));
+        *reinterpret_cast<u32x4_t *>(st + tl * kStageRow + 32 * mb + 16 * half + 8 * v) =
+            u32x4_t{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
       }
     wave_lds_fence();
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int n = sub + 8 * u + r8;
-      const uint4 w = *reinterpret_cast<const uint4 *>(st + (8 * u + r8) * kStageRow + 8 * c8);
+      const u32x4_t w = *reinterpret_cast<const u32x4_t *>(st + (8 * u + r8) * kStageRow + 8 * c8);
       if (n < hi) store_nt(op + (size_t)n * tok_stride, w);
     }
     wave_lds_fence();  // the next step's stage stores come after these loads
