@@ -105,8 +105,9 @@ def cpu_baseline(heads: int):
         "unit": "tokens/s",
         "cores": max(1, round(cpu / wall)),
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle, {heads} of {w.H} heads of one 720p/5s gated linear layer "
-                  f"(N={w.N}), {wall:.1f} s wall, scaled x{w.H // heads} to the full layer",
+        "sample": (f"fp64 numpy oracle, {heads} of {w.H} heads of one 720p/5s gated linear layer "
+                   f"(N={w.N}), {wall:.1f} s wall"
+                   + ("" if heads == w.H else f", scaled x{w.H / heads:g} to the full layer")),
         "cpu_seconds": round(cpu, 2),
         "cpu_model": model,
         "visible_cpus": len(os.sched_getaffinity(0)),
@@ -120,7 +121,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-legs", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--profile-pass", action="store_true",
                     help="for rocprofv3 counter runs: one untimed step, then a 1 GiB device copy whose "
                          "counter reading calibrates bytes; prints no JSON")

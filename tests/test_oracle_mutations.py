@@ -1,0 +1,67 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake (a dropped term, a wrong sign or index, a
+transposed operand, a wrong prefix) in a temporary copy of ``oracle/`` and runs
+``tests/test_oracle.py`` against that copy: at least one pin must fail. The
+repository's oracle is never modified; everything runs on the CPU.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (file under oracle/, original text, planted mistake)
+MUTATIONS = [
+    # RoPE: sign of the rotation, frequency exponent, coordinate decoding, band order
+    ("rope3d.py", "out[..., 0::2] = even * c - odd * s", "out[..., 0::2] = even * c + odd * s"),
+    ("rope3d.py", "(-2.0 * k / d)", "(-1.0 * k / d)"),
+    ("rope3d.py", "y = (n // Wg) % Hg", "y = (n // Hg) % Wg"),
+    ("rope3d.py", "for pos, d in zip((t, y, x), rope.bands)", "for pos, d in zip((t, x, y), rope.bands)"),
+    # bidirectional linear attention
+    ("linear_attention.py", 'denominator = np.einsum("bnhd,bhd->bnh", q_relu, k_sum)',
+     'denominator = np.einsum("bnhd,bhd->bnh", q_rope, k_sum)'),
+    ("linear_attention.py", "(denominator[..., None] + eps)", "np.maximum(denominator[..., None], eps)"),
+    ("linear_attention.py", 'kv = np.einsum("bnhd,bnhe->bhde", k_rope, v)', 'kv = np.einsum("bnhd,bnhe->bhed", k_rope, v)'),
+    ("linear_attention.py", "return q_relu, k_relu, rope3d_rotate(q_relu, theta), rope3d_rotate(k_relu, theta)",
+     "return q_relu, k_relu, rope3d_rotate(q_relu, theta), k_relu"),
+    ("linear_attention.py", "out = _sigmoid(g) * out\n    if return_state", "out = (1 - _sigmoid(g)) * out\n    if return_state"),
+    # chunked: exclusive instead of inclusive prefix, dropped key-sum input, wrong key sum, dropped gate
+    ("linear_attention.py",
+     '        num = np.einsum("bnhd,bhde->bnhe", q_rope[:, start:stop], kv)\n        den',
+     '        num = np.einsum("bnhd,bhde->bnhe", q_rope[:, start:stop], '
+     'kv - np.einsum("bnhd,bnhe->bhde", k_rope[:, start:stop], v[:, start:stop]))\n        den'),
+    ("linear_attention.py", "k_sum = np.zeros((B, H, D)) if ksum_in is None else np.array(ksum_in, dtype=np.float64)",
+     "k_sum = np.zeros((B, H, D))"),
+    ("linear_attention.py", "        k_sum = k_sum + k_relu[:, start:stop].sum(axis=1)",
+     "        k_sum = k_sum + q_relu[:, start:stop].sum(axis=1)"),
+    ("linear_attention.py", "        out[:, start:stop] = num / (den[..., None] + eps)\n    if g",
+     "        out[:, start:stop] = num / (den[..., None] + eps)\n    if False"),
+    # anchor: missing scale, softmax over the wrong axis
+    ("softmax_anchor.py", "logits = scale * (q[b, rr, h, :] @ kh.T)", "logits = (q[b, rr, h, :] @ kh.T)"),
+    ("softmax_anchor.py", "p = p / p.sum(axis=1, keepdims=True)", "p = p / p.sum(axis=0, keepdims=True)"),
+    # router: RMSNorm dropped, eps dropped, sum instead of mean
+    ("attnres_router.py", "normed = v / rms", "normed = v"),
+    ("attnres_router.py", "np.mean(v * v, axis=-1, keepdims=True) + eps", "np.mean(v * v, axis=-1, keepdims=True)"),
+    ("attnres_router.py", "np.mean(v * v, axis=-1, keepdims=True)", "np.sum(v * v, axis=-1, keepdims=True)"),
+]
+
+
+@pytest.mark.parametrize("fname,orig,bad", MUTATIONS, ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTATIONS)])
+def test_planted_mistake_fails_a_pin(tmp_path, fname, orig, bad):
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    (tmp_path / "tests").mkdir()
+    for f in ("conftest.py", "test_oracle.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
+    shutil.copy(os.path.join(ROOT, "synth.py"), tmp_path / "synth.py")
+    path = tmp_path / "oracle" / fname
+    src = path.read_text()
+    assert orig in src, f"mutation anchor not found in oracle/{fname}: {orig!r}"
+    path.write_text(src.replace(orig, bad, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle.py", "-q", "-x", "-p", "no:cacheprovider"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1, f"no pin caught the planted mistake ({bad!r}):\n{r.stdout[-2000:]}"
