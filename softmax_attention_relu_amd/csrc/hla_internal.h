@@ -44,10 +44,8 @@ struct RopeArgs {
 struct LinearPlan {
   int n_chunks;         // ceil(N / L)
   int chunk_len;        // L (min(L, N))
-  int slab_tokens;      // tokens per state-build work-group (multiple of 256)
-  int slabs_per_chunk;  // build work-groups per (b, head group, chunk)
-  int apply_tokens;     // tokens per apply work-group (multiple of 32)
-  int apply_per_chunk;  // apply work-groups per (b, head group, chunk)
+  int slabs_per_chunk;  // build work-groups per (b, head group, chunk); slab s takes tiles s, s+S, ...
+  int apply_per_chunk;  // apply work-groups per (b, head group, chunk); part p takes steps p, p+A, ...
   int ngroups;          // head groups of 4 (one head per wave)
   size_t part_offset, prefix_offset, total_bytes;  // workspace layout (bytes)
 };

@@ -20,6 +20,8 @@
 // tensors, and heads vary fastest across the grid. Memory traffic is the K/V
 // read of the build and the Q/G read and O write of the apply; the fp32
 // partial states are ~2% on top.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace hla {
@@ -81,7 +83,7 @@ struct Elem<false> {
 
 struct BuildArgs {
   const void *k, *v;
-  int N, H, L, n_chunks, slab_tokens, slabs_per_chunk, ngroups;
+  int N, H, L, n_chunks, slabs_per_chunk, ngroups;
   RopeArgs rope;
   float *part;  // [B*H][n_chunks*slabs_per_chunk][kStateFloats]
 };
@@ -136,7 +138,12 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 // ---------------------------------------------------------------------------
 // State build. Wave w of a work-group owns head 4*g + w of one slab and streams
-// its 64-token tiles with no work-group barrier. Lane (dc = lane%8,
+// its 64-token tiles with no work-group barrier. The tiles of a chunk are dealt
+// out to its S slabs in turn (slab s takes tiles s, s+S, s+2S, ...), so at any
+// moment the running work-groups read one contiguous window of K and V; giving
+// each slab a contiguous token range instead spaces the concurrent streams by
+// a fixed stride and loses up to a fifth of the bandwidth to uneven use of the
+// memory channels. Lane (dc = lane%8,
 // g = lane/8) loads dims 8*dc..+7 of tokens 8*g..+7: every load instruction
 // reads eight whole 128-byte token rows. The lane applies relu and RoPE, then
 // stores its 8x8 block transposed into the wave's LDS tiles (dim-major,
@@ -164,8 +171,6 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
   const int slab = slab_id - chunk * a.slabs_per_chunk;
   const int c_lo = chunk * a.L;
   const int c_hi = min(a.N, c_lo + a.L);
-  const int lo = c_lo + slab * a.slab_tokens;
-  const int hi = min(c_hi, lo + a.slab_tokens);
 
   const size_t tok_stride = (size_t)a.H * kD;
   const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD + dc * 8;
@@ -188,9 +193,11 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
 
   unsigned char *wl = lds_raw + wave * (kBF16 ? kWaveLds16 : kWaveLds32);
 
-  for (int base = lo; base < hi; base += kWTile) {
+  const int tile_step = a.slabs_per_chunk * kWTile;
+  for (int base = c_lo + slab * kWTile; base < c_hi; base += tile_step) {
+    const int hi = min(c_hi, base + kWTile);
     // Every load of the tile is issued before any use: token indices past the
-    // slab are clamped to its last token (always valid) and zeroed afterwards.
+    // tile are clamped to its last token (always valid) and zeroed afterwards.
     typename E::Chunk kr[8], vr[8];
     f32x2_t cs[kRope ? 8 : 1][4];
 #pragma unroll
@@ -361,8 +368,18 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
   const float *p = a.part + (size_t)bh * nsl * kStateFloats + idx;
   float *pre = a.prefix + (size_t)bh * a.n_chunks * kStateFloats + idx;
   for (int c = 0; c < a.n_chunks; ++c) {
+    // slabs are added in index order; the loads are issued eight at a time
+    const float *pc = p + (size_t)c * a.slabs_per_chunk * kStateFloats;
     float s = 0.f;
-    for (int i = 0; i < a.slabs_per_chunk; ++i) s += p[(size_t)(c * a.slabs_per_chunk + i) * kStateFloats];
+    int i = 0;
+    for (; i + 8 <= a.slabs_per_chunk; i += 8) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = pc[(size_t)(i + j) * kStateFloats];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += x[j];
+    }
+    for (; i < a.slabs_per_chunk; ++i) s += pc[(size_t)i * kStateFloats];
     run += s;
     pre[(size_t)c * kStateFloats] = run;
   }
@@ -377,7 +394,7 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
 struct ApplyArgs {
   const void *q, *g;
   void *o;
-  int N, H, L, n_chunks, apply_tokens, apply_per_chunk, ngroups;
+  int N, H, L, n_chunks, apply_per_chunk, ngroups;
   RopeArgs rope;
   float eps;
   const float *prefix;
@@ -388,8 +405,10 @@ __device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn
 __device__ __forceinline__ float sigmoid_exact(float x) { return 1.f / (1.f + expf(-x)); }
 
 // ---------------------------------------------------------------------------
-// Apply. Wave w of a work-group owns head 4*g + w of one token range inside a
-// chunk and walks it 32 tokens at a time. Q and G are loaded as whole 128-byte
+// Apply. Wave w of a work-group owns head 4*g + w of one part of a chunk and
+// walks it 32 tokens at a time; the 32-token steps of a chunk are dealt out to
+// its parts in turn (part p takes steps p, p+A, p+2A, ...), for the same reason
+// as the build's tiles. Q and G are loaded as whole 128-byte
 // rows (lane = token 8u + lane/8, dims 8*(lane%8)..+7) and turned into the
 // matrix-core lane layout through a per-wave LDS stage; O goes back through
 // the stage to whole-row non-temporal stores.
@@ -427,9 +446,9 @@ __global__ __launch_bounds__(256, (kRope && !kAligned) ? 1 : 2) void la_apply_bf
   const int part = pid - chunk * a.apply_per_chunk;
   const int c_lo = chunk * a.L;
   const int c_hi = min(a.N, c_lo + a.L);
-  const int lo = c_lo + part * a.apply_tokens;
-  const int hi = min(c_hi, lo + a.apply_tokens);
-  if (lo >= hi) return;
+  const int first = c_lo + part * kApplySub;
+  if (first >= c_hi) return;  // no work-group barrier follows
+  const int sub_step = a.apply_per_chunk * kApplySub;
 
   // A operand: P^T as hi + lo bf16 parts. Lane holds output row tl of block
   // mb (dim 32*mb + el) and reduction index d = 16*s + 8*half + t.
@@ -471,8 +490,9 @@ __global__ __launch_bounds__(256, (kRope && !kAligned) ? 1 : 2) void la_apply_bf
   uint16_t *op = reinterpret_cast<uint16_t *>(a.o) + head_base + 8 * c8;
   uint16_t *st = stage_all[wave];
 
-  for (int sub = lo; sub < hi; sub += kApplySub) {
-    // whole-row loads; tokens past the range read the last valid token
+  for (int sub = first; sub < c_hi; sub += sub_step) {
+    const int hi = min(c_hi, sub + kApplySub);
+    // whole-row loads; tokens past the step read the last valid token
     u32x4_t qrow[4], grow[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -591,9 +611,9 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
   const int part = pid - chunk * a.apply_per_chunk;
   const int c_lo = chunk * a.L;
   const int c_hi = min(a.N, c_lo + a.L);
-  const int lo = c_lo + part * a.apply_tokens;
-  const int hi = min(c_hi, lo + a.apply_tokens);
-  if (lo >= hi) return;
+  const int first = c_lo + part * kApplySub;
+  if (first >= c_hi) return;  // no work-group barrier follows
+  const int sub_step = a.apply_per_chunk * kApplySub;
 
   const float *P = a.prefix + ((size_t)bh * a.n_chunks + chunk) * kStateFloats;
   float sa[2][32];
@@ -611,7 +631,8 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
   const float *gp = a.g ? reinterpret_cast<const float *>(a.g) + head_base : nullptr;
   float *op = reinterpret_cast<float *>(a.o) + head_base;
 
-  for (int sub = lo; sub < hi; sub += kApplySub) {
+  for (int sub = first; sub < c_hi; sub += sub_step) {
+    const int hi = min(c_hi, sub + kApplySub);
     const int n = sub + tl;
     const bool valid = n < hi;
     const size_t row = (size_t)n * tok_stride;
@@ -700,20 +721,14 @@ LinearPlan plan_linear(int B, int N, int H, int chunk_tokens) {
   p.chunk_len = (int)L;
   p.n_chunks = (int)((N + L - 1) / L);
   p.ngroups = (H + kHeadsPerWG - 1) / kHeadsPerWG;
-  // about 512 work-groups per kernel (two per CU, one round), slabs and apply
-  // ranges whole multiples of the 64-token build tile and 32-token apply step
+  // about 512 work-groups per kernel (two per CU, one round); a chunk never
+  // gets more slabs than it has 64-token tiles, nor more parts than 32-token steps
   const long long per_chunk_groups = (long long)B * p.ngroups * p.n_chunks;
   const long long target = 512;
   long long split = (target + per_chunk_groups - 1) / per_chunk_groups;
   if (split < 1) split = 1;
-  long long slab = (L + split - 1) / split;
-  slab = ((slab + kWTile - 1) / kWTile) * kWTile;
-  p.slab_tokens = (int)slab;
-  p.slabs_per_chunk = (int)((L + slab - 1) / slab);
-  long long at = (L + split - 1) / split;
-  at = ((at + kApplySub - 1) / kApplySub) * kApplySub;
-  p.apply_tokens = (int)at;
-  p.apply_per_chunk = (int)((L + at - 1) / at);
+  p.slabs_per_chunk = (int)std::min(split, (L + kWTile - 1) / kWTile);
+  p.apply_per_chunk = (int)std::min(split, (L + kApplySub - 1) / kApplySub);
   const long long heads = (long long)B * H;
   const size_t part_bytes = (size_t)heads * p.n_chunks * p.slabs_per_chunk * kStateFloats * sizeof(float);
   const size_t prefix_bytes = (size_t)heads * p.n_chunks * kStateFloats * sizeof(float);
@@ -735,7 +750,6 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
   ba.H = a.H;
   ba.L = p.chunk_len;
   ba.n_chunks = p.n_chunks;
-  ba.slab_tokens = p.slab_tokens;
   ba.slabs_per_chunk = p.slabs_per_chunk;
   ba.ngroups = p.ngroups;
   ba.rope = a.rope;
@@ -770,7 +784,6 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
   aa.H = a.H;
   aa.L = p.chunk_len;
   aa.n_chunks = p.n_chunks;
-  aa.apply_tokens = p.apply_tokens;
   aa.apply_per_chunk = p.apply_per_chunk;
   aa.ngroups = p.ngroups;
   aa.rope = a.rope;
