@@ -30,6 +30,7 @@ RopeArgs make_rope(const hla_rope3d *r) {
   ra.d_w = r->d_w;
   ra.hw = (uint32_t)r->grid_h * (uint32_t)r->grid_w;
   ra.w = (uint32_t)r->grid_w;
+  ra.h = (uint32_t)r->grid_h;
   ra.div_hw = make_fastdiv(ra.hw);
   ra.div_w = make_fastdiv(ra.w);
   ra.cs_t = r->cs_t;

@@ -34,7 +34,7 @@ struct RopeArgs {
   int enabled;
   int aligned;           // band widths multiples of 8 and 16-byte aligned tables
   int d_t, d_h, d_w;
-  uint32_t hw, w;        // grid_h * grid_w, grid_w
+  uint32_t hw, w, h;     // grid_h * grid_w, grid_w, grid_h
   FastDiv div_hw, div_w;
   const float *cs_t, *cs_h, *cs_w;
 };

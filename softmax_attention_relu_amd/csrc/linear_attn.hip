@@ -127,6 +127,61 @@ struct ChunkRope {
   }
 };
 
+// RoPE of the state build for an aligned 8-dim chunk. A build lane rotates 8
+// consecutive tokens, so it reads (cos, sin) from its band's table for the
+// first of them and moves to the next position with the angle-addition
+// identity: cos(a+u) = cos a cos u - sin a sin u, sin(a+u) = sin a cos u +
+// cos a sin u, u being the band's unit angle (row 1 of the h or w table, whose
+// rows start at position 0). A position that does not move by exactly one (a
+// new row or frame, and the t band, whose table may start at an offset) is read
+// from the table again. At most seven steps lie between a table read and its
+// use, a few ulp on cos and sin.
+struct RopeWalk {
+  const float *col;
+  int stride, band;
+  bool can_step;
+  f32x2_t unit[4];
+  __device__ __forceinline__ void fetch(uint32_t pos, f32x2_t cs[4]) const {
+    const float *q = col + (size_t)pos * stride;
+    const f32x4_t a = *reinterpret_cast<const f32x4_t *>(q);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t *>(q + 4);
+    cs[0] = f32x2_t{a.x, a.y};
+    cs[1] = f32x2_t{a.z, a.w};
+    cs[2] = f32x2_t{b.x, b.y};
+    cs[3] = f32x2_t{b.z, b.w};
+  }
+  __device__ __forceinline__ void init(const RopeArgs &r, int chunk) {
+    const RopePair p = rope_pair(r, 4 * chunk);
+    col = p.col;
+    stride = p.stride;
+    band = p.band;
+    can_step = band != 0 && (band == 1 ? r.h : r.w) >= 2;
+    if (can_step) {
+      fetch(1, unit);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) unit[j] = f32x2_t{1.f, 0.f};
+    }
+  }
+  __device__ __forceinline__ uint32_t coord(const TokenPos &tp) const {
+    return band == 0 ? tp.t : (band == 1 ? tp.y : tp.x);
+  }
+  // cs holds the pairs at position `from`; leave them at position `to`
+  __device__ __forceinline__ void advance(uint32_t from, uint32_t to, f32x2_t cs[4]) const {
+    if (to == from) return;
+    if (can_step && to == from + 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float c = cs[j].x * unit[j].x - cs[j].y * unit[j].y;
+        const float sn = cs[j].y * unit[j].x + cs[j].x * unit[j].y;
+        cs[j] = f32x2_t{c, sn};
+      }
+    } else {
+      fetch(to, cs);
+    }
+  }
+};
+
 // Orders this wave's LDS stores before its later LDS loads (and the reverse)
 // without a work-group barrier: LDS requests of one wave are served in order,
 // the fence keeps the compiler from moving them across.
@@ -177,8 +232,11 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
   const T *kp = reinterpret_cast<const T *>(a.k) + head_base;
   const T *vp = reinterpret_cast<const T *>(a.v) + head_base;
 
-  ChunkRope<kAligned> cr;
-  if constexpr (kRope) cr.init(a.rope, dc);
+  // aligned bands: walk the positions; otherwise look every pair up
+  RopeWalk walk;
+  ChunkRope<false> cr;
+  if constexpr (kRope && kAligned) walk.init(a.rope, dc);
+  if constexpr (kRope && !kAligned) cr.init(a.rope, dc);
 
   float zacc[8];
 #pragma unroll
@@ -199,61 +257,26 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
     // Every load of the tile is issued before any use: token indices past the
     // tile are clamped to its last token (always valid) and zeroed afterwards.
     typename E::Chunk kr[8], vr[8];
-    f32x2_t cs[kRope ? 8 : 1][4];
+    f32x2_t cs[(kRope && !kAligned) ? 8 : 1][4];
+    f32x2_t cur[4];
+    uint32_t cpos = 0;
+    // V first: it is transposed into LDS (freeing its registers) while K lands
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int n = min(base + 8 * g + r, hi - 1);
-      kr[r] = E::load(kp + (size_t)n * tok_stride);
-      vr[r] = E::load(vp + (size_t)n * tok_stride);
-    }
-    if constexpr (kRope) {
+    for (int r = 0; r < 8; ++r) vr[r] = E::load(vp + (size_t)min(base + 8 * g + r, hi - 1) * tok_stride);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) kr[r] = E::load(kp + (size_t)min(base + 8 * g + r, hi - 1) * tok_stride);
+    if constexpr (kRope && kAligned) {
+      cpos = walk.coord(token_pos(a.rope, (uint32_t)min(base + 8 * g, hi - 1)));
+      walk.fetch(cpos, cur);
+    } else if constexpr (kRope) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) cr.get(token_pos(a.rope, (uint32_t)min(base + 8 * g + r, hi - 1)), cs[r]);
     }
-    // relu, key sum, rotation; bf16 tiles pack token pairs right away
-    float c[kBF16 ? 1 : 8][8];
-    uint32_t pk[8][4];
-    float prev[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const bool valid = base + 8 * g + r < hi;
-      if (!valid) {
-        kr[r] = E::zero();
-        vr[r] = E::zero();
-      }
-      float x[8];
-      E::unpack(kr[r], x);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[i] = fmaxf(x[i], 0.f);
-        zacc[i] += x[i];
-      }
-      if constexpr (kRope) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], cs[r][j]);
-      }
-      if constexpr (kBF16) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (r & 1)
-            pk[i][r >> 1] = pack_bf16(prev[i], x[i]);
-          else
-            prev[i] = x[i];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[r][i] = x[i];
-      }
-    }
+    for (int r = 0; r < 8; ++r)
+      if (base + 8 * g + r >= hi) vr[r] = E::zero();
     if constexpr (kBF16) {
-      uint16_t *cT = reinterpret_cast<uint16_t *>(wl);
-      uint16_t *vT = cT + kD * kWRow16;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = 8 * dc + i;
-        *reinterpret_cast<uint4 *>(cT + row * kWRow16 + 8 * (g ^ gran_swz(row))) =
-            make_uint4(pk[i][0], pk[i][1], pk[i][2], pk[i][3]);
-      }
+      uint16_t *vT = reinterpret_cast<uint16_t *>(wl) + kD * kWRow16;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t wd[8];
@@ -273,6 +296,70 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
         const int row = 8 * dc + i;
         *reinterpret_cast<uint4 *>(vT + row * kWRow16 + 8 * (g ^ gran_swz(row))) = w;
       }
+    } else {
+      float *vT = reinterpret_cast<float *>(wl) + kD * kWRow32;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float vv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          float x[8];
+          E::unpack(vr[r], x);
+          vv[r] = x[i];
+        }
+        float *dst = vT + (8 * dc + i) * kWRow32 + 8 * g;
+        *reinterpret_cast<float4 *>(dst) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+        *reinterpret_cast<float4 *>(dst + 4) = make_float4(vv[4], vv[5], vv[6], vv[7]);
+      }
+    }
+    // relu, key sum, rotation; bf16 tiles pack token pairs right away
+    float c[kBF16 ? 1 : 8][8];
+    uint32_t pk[8][4];
+    float prev[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (base + 8 * g + r >= hi) kr[r] = E::zero();
+      float x[8];
+      E::unpack(kr[r], x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i] = fmaxf(x[i], 0.f);
+        zacc[i] += x[i];
+      }
+      if constexpr (kRope && kAligned) {
+        if (r > 0) {
+          const uint32_t np = walk.coord(token_pos(a.rope, (uint32_t)min(base + 8 * g + r, hi - 1)));
+          walk.advance(cpos, np, cur);
+          cpos = np;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], cur[j]);
+      } else if constexpr (kRope) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rotate(x[2 * j], x[2 * j + 1], cs[r][j]);
+      }
+      if constexpr (kBF16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (r & 1)
+            pk[i][r >> 1] = pack_bf16(prev[i], x[i]);
+          else
+            prev[i] = x[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[r][i] = x[i];
+      }
+    }
+    if constexpr (kBF16) {
+      uint16_t *cT = reinterpret_cast<uint16_t *>(wl);
+      const uint16_t *vT = cT + kD * kWRow16;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 8 * dc + i;
+        *reinterpret_cast<uint4 *>(cT + row * kWRow16 + 8 * (g ^ gran_swz(row))) =
+            make_uint4(pk[i][0], pk[i][1], pk[i][2], pk[i][3]);
+      }
       wave_lds_fence();
       const int r0 = tl, r1 = 32 + tl;
 #pragma unroll
@@ -289,25 +376,12 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
       }
     } else {
       float *cT = reinterpret_cast<float *>(wl);
-      float *vT = cT + kD * kWRow32;
+      const float *vT = cT + kD * kWRow32;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float *dst = cT + (8 * dc + i) * kWRow32 + 8 * g;
         *reinterpret_cast<float4 *>(dst) = make_float4(c[0][i], c[1][i], c[2][i], c[3][i]);
         *reinterpret_cast<float4 *>(dst + 4) = make_float4(c[4][i], c[5][i], c[6][i], c[7][i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float vv[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          float x[8];
-          E::unpack(vr[r], x);
-          vv[r] = x[i];
-        }
-        float *dst = vT + (8 * dc + i) * kWRow32 + 8 * g;
-        *reinterpret_cast<float4 *>(dst) = make_float4(vv[0], vv[1], vv[2], vv[3]);
-        *reinterpret_cast<float4 *>(dst + 4) = make_float4(vv[4], vv[5], vv[6], vv[7]);
       }
       wave_lds_fence();
       const float *a0p = cT + tl * kWRow32 + half, *a1p = cT + (32 + tl) * kWRow32 + half;
