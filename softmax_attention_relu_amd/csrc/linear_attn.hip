@@ -472,6 +472,48 @@ struct ApplyArgs {
   RopeArgs rope;
   float eps;
   const float *prefix;
+  int tab_t, tab_h, tab_w;  // floats in each band's table (LDS-staged RoPE)
+};
+
+// RoPE variants of the bf16 apply
+constexpr int kRopeNone = 0;    // no rotation
+constexpr int kRopePair = 1;    // any band widths: each pair looked up in global memory
+constexpr int kRopeGlobal = 2;  // band widths multiples of 8: two 16-byte global loads per 8 dims
+constexpr int kRopeLds = 3;     // as kRopeGlobal, from a copy of the tables in LDS
+constexpr int kTabLdsFloats = 9216;  // largest table set staged in LDS (36 KB)
+
+extern __shared__ __align__(16) float la_tab_lds[];
+
+// (cos, sin) of the four pairs of one 8-dim chunk from the LDS copy of the
+// tables, laid out [t table | h table | w table].
+struct ChunkRopeLds {
+  int off, stride, band;
+  __device__ __forceinline__ void init(const RopeArgs &r, const ApplyArgs &a, int chunk) {
+    const int two_p = 8 * chunk;
+    if (two_p < r.d_t) {
+      off = two_p;
+      stride = r.d_t;
+      band = 0;
+    } else if (two_p < r.d_t + r.d_h) {
+      off = a.tab_t + two_p - r.d_t;
+      stride = r.d_h;
+      band = 1;
+    } else {
+      off = a.tab_t + a.tab_h + two_p - r.d_t - r.d_h;
+      stride = r.d_w;
+      band = 2;
+    }
+  }
+  __device__ __forceinline__ void get(const TokenPos &tp, f32x2_t cs[4]) const {
+    const uint32_t pos = band == 0 ? tp.t : (band == 1 ? tp.y : tp.x);
+    const int i = off + (int)pos * stride;
+    const f32x4_t a = *reinterpret_cast<const f32x4_t *>(&la_tab_lds[i]);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t *>(&la_tab_lds[i + 4]);
+    cs[0] = f32x2_t{a.x, a.y};
+    cs[1] = f32x2_t{a.z, a.w};
+    cs[2] = f32x2_t{b.x, b.y};
+    cs[3] = f32x2_t{b.z, b.w};
+  }
 };
 
 // bf16 outputs: hardware exp and reciprocal (about 1 ulp); exactly 1/2 at 0.
@@ -502,8 +544,9 @@ __device__ __forceinline__ void store_nt(uint16_t *p, u32x4_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
 }
 
-template <bool kRope, bool kAligned, bool kGate>
-__global__ __launch_bounds__(256, (kRope && !kAligned) ? 1 : 2) void la_apply_bf16_kernel(ApplyArgs a) {
+template <int kRopeMode, bool kGate>
+__global__ __launch_bounds__(256, kRopeMode == kRopePair ? 1 : 2) void la_apply_bf16_kernel(ApplyArgs a) {
+  constexpr bool kRope = kRopeMode != kRopeNone;
   __shared__ __align__(16) uint16_t stage_all[kHeadsPerWG][kApplySub * kStageRow];
 
   const int tid = threadIdx.x;
@@ -512,17 +555,29 @@ __global__ __launch_bounds__(256, (kRope && !kAligned) ? 1 : 2) void la_apply_bf
   const int r8 = lane >> 3, c8 = lane & 7;
   const int hgroup = blockIdx.x % a.ngroups;
   const int pid = blockIdx.x / a.ngroups;
-  const int h = kHeadsPerWG * hgroup + wave;
-  if (h >= a.H) return;  // no work-group barrier follows
-  const int b = blockIdx.y;
-  const int bh = b * a.H + h;
   const int chunk = pid / a.apply_per_chunk;
   const int part = pid - chunk * a.apply_per_chunk;
   const int c_lo = chunk * a.L;
   const int c_hi = min(a.N, c_lo + a.L);
   const int first = c_lo + part * kApplySub;
-  if (first >= c_hi) return;  // no work-group barrier follows
+  if (first >= c_hi) return;  // the same for the whole work-group
   const int sub_step = a.apply_per_chunk * kApplySub;
+  if constexpr (kRopeMode == kRopeLds) {
+    // copy the three tables into LDS (each a multiple of 8 floats)
+    const int n4 = (a.tab_t + a.tab_h + a.tab_w) / 4;
+    for (int i = tid; i < n4; i += 256) {
+      const int f = 4 * i;
+      const float *src = f < a.tab_t ? a.rope.cs_t + f
+                                      : (f < a.tab_t + a.tab_h ? a.rope.cs_h + (f - a.tab_t)
+                                                               : a.rope.cs_w + (f - a.tab_t - a.tab_h));
+      *reinterpret_cast<f32x4_t *>(&la_tab_lds[f]) = *reinterpret_cast<const f32x4_t *>(src);
+    }
+    __syncthreads();
+  }
+  const int h = kHeadsPerWG * hgroup + wave;
+  if (h >= a.H) return;  // no work-group barrier follows
+  const int b = blockIdx.y;
+  const int bh = b * a.H + h;
 
   // A operand: P^T as hi + lo bf16 parts. Lane holds output row tl of block
   // mb (dim 32*mb + el) and reduction index d = 16*s + 8*half + t.
@@ -551,8 +606,12 @@ __global__ __launch_bounds__(256, (kRope && !kAligned) ? 1 : 2) void la_apply_bf
 #pragma unroll
     for (int t = 0; t < 8; ++t) zr[s][t] = P[kD * kD + 16 * s + 8 * half + t];
 
-  ChunkRope<kAligned> cr[4];
-  if constexpr (kRope) {
+  ChunkRope<kRopeMode != kRopePair> cr[4];
+  ChunkRopeLds crl[4];
+  if constexpr (kRopeMode == kRopeLds) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) crl[s].init(a.rope, a, 2 * s + half);
+  } else if constexpr (kRope) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) cr[s].init(a.rope, 2 * s + half);
   }
@@ -578,7 +637,12 @@ __global__ __launch_bounds__(256, (kRope && !kAligned) ? 1 : 2) void la_apply_bf
     if constexpr (kRope) {
       const TokenPos tp = token_pos(a.rope, (uint32_t)min(sub + tl, hi - 1));
 #pragma unroll
-      for (int s = 0; s < 4; ++s) cr[s].get(tp, cs[s]);
+      for (int s = 0; s < 4; ++s) {
+        if constexpr (kRopeMode == kRopeLds)
+          crl[s].get(tp, cs[s]);
+        else
+          cr[s].get(tp, cs[s]);
+      }
     }
     // q rows -> lane layout
 #pragma unroll
@@ -779,12 +843,13 @@ hipError_t launch_build_any(const RopeArgs &r, dim3 grid, const BuildArgs &ba, h
   return launch_build<kBF16, true, false>(grid, ba, stream);
 }
 
-template <bool kRope, bool kAligned>
+template <int kRopeMode>
 void launch_apply_bf16(bool gate, dim3 grid, const ApplyArgs &aa, hipStream_t stream) {
+  const size_t lds = kRopeMode == kRopeLds ? (size_t)(aa.tab_t + aa.tab_h + aa.tab_w) * sizeof(float) : 0;
   if (gate)
-    hipLaunchKernelGGL((la_apply_bf16_kernel<kRope, kAligned, true>), grid, dim3(256), 0, stream, aa);
+    hipLaunchKernelGGL((la_apply_bf16_kernel<kRopeMode, true>), grid, dim3(256), lds, stream, aa);
   else
-    hipLaunchKernelGGL((la_apply_bf16_kernel<kRope, kAligned, false>), grid, dim3(256), 0, stream, aa);
+    hipLaunchKernelGGL((la_apply_bf16_kernel<kRopeMode, false>), grid, dim3(256), lds, stream, aa);
 }
 
 }  // namespace
@@ -863,15 +928,24 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
   aa.rope = a.rope;
   aa.eps = a.eps;
   aa.prefix = prefix;
+  aa.tab_t = aa.tab_h = aa.tab_w = 0;
+  if (a.rope.enabled) {
+    aa.tab_t = (int)((uint32_t)a.N / a.rope.hw) * a.rope.d_t;
+    aa.tab_h = (int)a.rope.h * a.rope.d_h;
+    aa.tab_w = (int)a.rope.w * a.rope.d_w;
+  }
   const dim3 agrid(p.n_chunks * p.apply_per_chunk * p.ngroups, a.B);
   if (dt == HLA_BF16) {
     const bool gate = a.g != nullptr;
+    const int tab_floats = aa.tab_t + aa.tab_h + aa.tab_w;
     if (!a.rope.enabled)
-      launch_apply_bf16<false, false>(gate, agrid, aa, stream);
-    else if (a.rope.aligned)
-      launch_apply_bf16<true, true>(gate, agrid, aa, stream);
+      launch_apply_bf16<kRopeNone>(gate, agrid, aa, stream);
+    else if (!a.rope.aligned)
+      launch_apply_bf16<kRopePair>(gate, agrid, aa, stream);
+    else if (tab_floats <= kTabLdsFloats)
+      launch_apply_bf16<kRopeLds>(gate, agrid, aa, stream);
     else
-      launch_apply_bf16<true, false>(gate, agrid, aa, stream);
+      launch_apply_bf16<kRopeGlobal>(gate, agrid, aa, stream);
   } else
     hipLaunchKernelGGL(la_apply_f32_kernel, agrid, dim3(256), 0, stream, aa);
   return hipGetLastError();

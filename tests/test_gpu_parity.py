@@ -181,6 +181,23 @@ def test_chunked_small_shapes(dtype, N, L):
     assert normwise(host(kso), ks_ref) <= 1e-5
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("grid,bands,chunk", [
+    ((6, 10, 10), (18, 22, 24), 0),     # band widths not multiples of 8: every pair looked up alone
+    ((6, 10, 10), (18, 22, 24), 250),
+    ((600, 1, 1), (16, 24, 24), 0),     # 9648 table floats: too large to stage in LDS
+    ((600, 1, 1), (16, 24, 24), 128),
+    ((12, 5, 10), (16, 24, 24), 0),     # staged in LDS
+])
+def test_linear_rope_table_paths(dtype, grid, bands, chunk):
+    N = grid[0] * grid[1] * grid[2]
+    x = {nm: synth.randn(500 + N + chunk, (1, N, 3, 64), dtype=dtype, stream=i) for i, nm in enumerate("qkvg")}
+    got = host(run_linear(x, grid, chunk=chunk, bands=bands))
+    ref, _, _ = oracle_linear_per_head(x, grid, chunk=chunk, bands=bands)
+    err = normwise(got, ref)
+    assert err <= tol(dtype), err
+
+
 def test_chunked_resume_and_aliasing():
     """Two calls carrying the state (second with t_offset, state updated in place) equal one call."""
     grid, L = (10, 10, 10), 200
