@@ -8,7 +8,7 @@
 //              tokens zero-padded to a multiple of 64 and permuted inside each
 //              group of 16 so that every matrix-core operand of the P.V product
 //              is one contiguous 16-byte LDS read (see kernel comment).
-//   anchor_fwd online-softmax attention. A work-group of 8 waves owns 256
+//   anchor_fwd online-softmax attention. A work-group of 16 waves owns 512
 //              query rows of one (b, h); wave w owns 32 rows. Per 64-key tile:
 //                S^T = K Q^T   (A = K rows from LDS, B = Q^T held in registers)
 //                softmax update in the exp2 domain, lane-local: the score layout
@@ -17,10 +17,12 @@
 //                score registers, rounded to bf16)
 //              K and V^T tiles are double-buffered in LDS; the next tile's
 //              global loads are issued before the current tile's products.
-// 128 registers per lane keep every accumulator in VGPRs and let four waves
-// per SIMD interleave their softmax (vector ALU) with their products (matrix
-// cores); the tile's row max is combined across the two lane halves with
-// v_permlane32_swap.
+// At most 128 registers per lane keep every accumulator in VGPRs with four
+// waves per SIMD; the tile's row max is combined across the two lane halves
+// with v_permlane32_swap. On this chip the plain vector ALU work of the
+// softmax (one FMA, one max and half a conversion per score) does not overlap
+// the matrix-core work much, while exponentials largely do; that, not the
+// matrix cores, sets the kernel's speed.
 // The running max is refreshed lazily: rows keep their reference max until a
 // tile exceeds it by more than 8 (log2 units), so exponentials stay <= 2^8
 // and the O / row-sum rescale is almost never taken. The normaliser uses the
@@ -35,7 +37,7 @@ constexpr int kBK = 64;            // keys per tile
 constexpr int kKRow = kD + 8;      // bf16 per LDS row of K (144 bytes)
 constexpr int kVRow = kBK + 8;     // bf16 per LDS row of V^T (144 bytes)
 constexpr float kLazy = 8.0f;      // lazy max threshold, log2 units
-constexpr int kWaves = 8;          // waves per work-group, 32 query rows each
+constexpr int kWaves = 16;         // waves per work-group, 32 query rows each
 constexpr int kMinWaves = 4;       // waves per SIMD the forward kernel is compiled for
 
 // Key position inside a group of 16 with bits 2 and 3 swapped. With this
@@ -100,7 +102,11 @@ struct FwdArgs {
   float c;  // scale * log2(e)
 };
 
-template <int RB, int WAVES, int MINW>
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// The row sum adds the bf16-rounded P with v_dot2 (two terms per
+// instruction): the normaliser uses the same weights as the P.V product.
+template <int WAVES, int MINW>
 __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a) {
   constexpr int kThreads = 64 * WAVES;
   // 16-byte chunks of K (and of V^T) per thread per tile: 512 chunks each
@@ -114,23 +120,22 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
   const int half = lane >> 5, tl = lane & 31;
   const int bh = blockIdx.y;
   const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const int q0 = blockIdx.x * (32 * RB * WAVES) + wave * (32 * RB);
+  const int q0 = blockIdx.x * (32 * WAVES) + wave * 32;
 
   const size_t tok_stride = (size_t)a.H * kD;
   const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD;
   const uint16_t *kp = a.k + head_base;
   const uint16_t *vtp = a.vt + (size_t)bh * kD * a.npad;
 
-  // Q^T operands: row q0 + 32*rb + tl, dims 16*s + 8*half .. +7
-  bf16x8_t qb[RB][4];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int n = q0 + 32 * rb + tl;
+  // Q^T operands: row q0 + tl, dims 16*s + 8*half .. +7
+  bf16x8_t qb[4];
+  {
+    const int n = q0 + tl;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint4 w = make_uint4(0, 0, 0, 0);
       if (n < a.N) w = *reinterpret_cast<const uint4 *>(a.q + head_base + (size_t)n * tok_stride + 16 * s + 8 * half);
-      qb[rb][s] = __builtin_bit_cast(bf16x8_t, w);
+      qb[s] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
 
@@ -138,10 +143,11 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
   // chunks spread over the work-group
   uint4 kreg[kLoads], vreg[kLoads];
   auto load_tile = [&](int t) {
+    if (tid >= kLoaders) return;
     const int n0 = t * kBK;
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
-      const int c = min(tid, kLoaders - 1) + kLoaders * r;
+      const int c = tid + kLoaders * r;
       const int row = c >> 3, ch = c & 7;
       const int n = n0 + row;
       kreg[r] = n < a.N ? *reinterpret_cast<const uint4 *>(kp + (size_t)n * tok_stride + 8 * ch) : make_uint4(0, 0, 0, 0);
@@ -159,19 +165,12 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     }
   };
 
-  f32x16_t oacc[RB][2];
+  f32x16_t oacc[2];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[rb][mb][i] = 0.f;
-  float mref[RB], lsum[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    mref[rb] = -INFINITY;
-    lsum[rb] = 0.f;
-  }
+    for (int i = 0; i < 16; ++i) oacc[mb][i] = 0.f;
+  float mref = -INFINITY, lsum = 0.f;
 
   const int ntiles = (a.N + kBK - 1) / kBK;
   load_tile(0);
@@ -182,22 +181,18 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     if (t + 1 < ntiles) load_tile(t + 1);
 
     // S^T = K Q^T for the 64 keys of this tile
-    f32x16_t sacc[RB][2];
+    f32x16_t sacc[2];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[rb][kb][i] = 0.f;
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const bf16x8_t kv =
             *reinterpret_cast<const bf16x8_t *>(&ks[buf][(32 * kb + tl) * kKRow + 16 * s + 8 * half]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          sacc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qb[rb][s], sacc[rb][kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qb[s], sacc[kb], 0, 0, 0);
       }
 
     // mask keys past the end (last tile only)
@@ -207,53 +202,59 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = t * kBK + 32 * kb + 8 * i + 4 * half + j;
-            if (key >= a.N) {
-#pragma unroll
-              for (int rb = 0; rb < RB; ++rb) sacc[rb][kb][4 * i + j] = -INFINITY;
-            }
-          }
+          for (int j = 0; j < 4; ++j)
+            if (t * kBK + 32 * kb + 8 * i + 4 * half + j >= a.N) sacc[kb][4 * i + j] = -INFINITY;
     }
 
-    // online softmax (exp2 domain), lazy reference max
-    bf16x8_t pb[RB][2][2];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float mx = sacc[rb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[rb][kb][i]);
-      mx = max_halves(mx);
-      const float mt = mx * a.c;
-      const bool bump = mt > mref[rb] + kLazy;
-      if (__any(bump)) {
-        const float mnew = bump ? mt : mref[rb];
-        const float f = exp2f(mref[rb] - mnew);
-        mref[rb] = mnew;
-        lsum[rb] *= f;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[rb][mb][i] *= f;
-      }
-      const float nm = -mref[rb];
+    // online softmax (exp2 domain); ts is this lane's share of the tile's row sum
+    bf16x8_t pb[2][2];
+    float ts;
+    auto exps = [&](float nm) {
+      ts = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float p[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][i], a.c, nm));
-          lsum[rb] += p[i];
+          p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], a.c, nm));
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          pb[rb][kb][u] = __builtin_bit_cast(
-              bf16x8_t, make_uint4(pack_bf16(p[8 * u + 0], p[8 * u + 1]), pack_bf16(p[8 * u + 2], p[8 * u + 3]),
-                                   pack_bf16(p[8 * u + 4], p[8 * u + 5]), pack_bf16(p[8 * u + 6], p[8 * u + 7])));
+        for (int u = 0; u < 2; ++u) {
+          const uint4 w = make_uint4(pack_bf16(p[8 * u + 0], p[8 * u + 1]), pack_bf16(p[8 * u + 2], p[8 * u + 3]),
+                                     pack_bf16(p[8 * u + 4], p[8 * u + 5]), pack_bf16(p[8 * u + 6], p[8 * u + 7]));
+          pb[kb][u] = __builtin_bit_cast(bf16x8_t, w);
+          const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+          ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), one, ts, false);
+          ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), one, ts, false);
+          ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), one, ts, false);
+          ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), one, ts, false);
+        }
       }
+    };
+    auto row_max = [&]() {
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      return max_halves(mx) * a.c;
+    };
+    auto rescale = [&](float mnew) {
+      const float f = exp2f(mref - mnew);
+      mref = mnew;
+      lsum *= f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[mb][i] *= f;
+    };
+    {
+      const float mt = row_max();
+      const bool bump = mt > mref + kLazy;
+      if (__any(bump)) rescale(bump ? mt : mref);
+      exps(-mref);
     }
+    lsum += ts;
 
     // O^T += V^T P^T
 #pragma unroll
@@ -264,9 +265,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
         for (int u = 0; u < 2; ++u) {
           const bf16x8_t vv =
               *reinterpret_cast<const bf16x8_t *>(&vs[buf][(32 * mb + tl) * kVRow + 32 * kb + 16 * u + 8 * half]);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            oacc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[rb][kb][u], oacc[rb][mb], 0, 0, 0);
+          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kb][u], oacc[mb], 0, 0, 0);
         }
 
     if (t + 1 < ntiles) {
@@ -275,32 +274,29 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     }
   }
 
-  // normalise, gate, store: lane holds row tl of block rb, dims 32*mb + 8*i + 4*half + j
+  // normalise, gate, store: lane holds row tl, dims 32*mb + 8*i + 4*half + j
+  const int n = q0 + tl;
+  const float l = lsum + __shfl_xor(lsum, 32);
+  const float inv = 1.f / l;
+  if (n < a.N) {
+    const size_t row = head_base + (size_t)n * tok_stride;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int n = q0 + 32 * rb + tl;
-    const float l = lsum[rb] + __shfl_xor(lsum[rb], 32);
-    const float inv = 1.f / l;
-    if (n < a.N) {
-      const size_t row = head_base + (size_t)n * tok_stride;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int i = 0; i < 4; ++i) {
+        const size_t off = row + 32 * mb + 8 * i + 4 * half;
+        float y[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const size_t off = row + 32 * mb + 8 * i + 4 * half;
-          float y[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = oacc[rb][mb][4 * i + j] * inv;
-          if (a.g) {
-            const uint2 gw = *reinterpret_cast<const uint2 *>(a.g + off);
-            y[0] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_lo(gw.x)));
-            y[1] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_hi(gw.x)));
-            y[2] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_lo(gw.y)));
-            y[3] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_hi(gw.y)));
-          }
-          *reinterpret_cast<uint2 *>(a.o + off) = make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
+        for (int j = 0; j < 4; ++j) y[j] = oacc[mb][4 * i + j] * inv;
+        if (a.g) {
+          const uint2 gw = *reinterpret_cast<const uint2 *>(a.g + off);
+          y[0] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_lo(gw.x)));
+          y[1] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_hi(gw.x)));
+          y[2] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_lo(gw.y)));
+          y[3] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_hi(gw.y)));
         }
-    }
+        *reinterpret_cast<uint2 *>(a.o + off) = make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
+      }
   }
 }
 
@@ -324,7 +320,6 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  constexpr int RB = 1, WAVES = kWaves, MINW = kMinWaves;
   FwdArgs fa;
   fa.q = reinterpret_cast<const uint16_t *>(a.q);
   fa.k = reinterpret_cast<const uint16_t *>(a.k);
@@ -335,9 +330,8 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   fa.H = a.H;
   fa.npad = npad;
   fa.c = a.scale * 1.4426950408889634f;
-  const int rows = 32 * RB * WAVES;
-  hipLaunchKernelGGL((anchor_fwd_kernel<RB, WAVES, MINW>), dim3((a.N + rows - 1) / rows, heads), dim3(64 * WAVES), 0,
-                     stream, fa);
+  hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves>), dim3((a.N + 32 * kWaves - 1) / (32 * kWaves), heads),
+                     dim3(64 * kWaves), 0, stream, fa);
   return hipGetLastError();
 }
 
