@@ -246,8 +246,8 @@ def main() -> int:
     rt_bytes = rw0.B * rw0.T * rw0.C * 2 * (rw0.S + 1)
     rt_gbs = rt_bytes / (rt_ms * 1e-3) / 1e9
 
-    # anchor_fwd_kernel launches 512 threads per 256 query rows of one head
-    anchor_threads = -(-aw.N // 256) * aw.B * aw.H * 512
+    # anchor_fwd_kernel launches 1024 threads per 512 query rows of one head
+    anchor_threads = -(-aw.N // 512) * aw.B * aw.H * 1024
     anchor_traffic = _traffic("anchor_fwd_kernel", anchor_threads, _src_hash("anchor.hip"))
     out = {
         "metric": "linear-attn tokens/s & HBM GB/s at 720p/5s shape; anchor MFMA util %",
