@@ -322,6 +322,55 @@ def main() -> int:
         del cx, ws
         torch.cuda.empty_cache()
 
+        # ---------------- streaming leg: the 720p/60s sequence block by block (ten frames per
+        # block), two denoising calls per block that read the cache, the second also commits the
+        # block; a cond/uncond pair (B = 2). Block inputs are drawn once and reused by every block.
+        sb, steps, frames = 2, 2, 10
+        hw = cw.grid[1] * cw.grid[2]
+        nblk = -(-cw.grid[0] // frames)
+        log("[bench] streaming 720p/60s leg (B=2, two steps per block): drawing inputs")
+        blk = {}
+        for L in sorted({min(frames, cw.grid[0] - frames * b) * hw for b in range(nblk)}):
+            blk[L] = {nm: dev(synth.randn(6, (sb, L, cw.H, 64), stream=i)) for i, nm in enumerate("qkv")}
+            blk[L]["o"] = torch.empty_like(blk[L]["q"])
+        ropes = [hla.Rope3D((min(frames, cw.grid[0] - frames * b), cw.grid[1], cw.grid[2]), cw.bands, cw.base,
+                            t_offset=frames * b) for b in range(nblk)]
+        lmax = frames * hw
+        ws = torch.empty(hla.hla_linear_attn_chunked_workspace(sb, lmax, cw.H, cw.D, lmax), dtype=torch.uint8,
+                         device="cuda")
+        kv = torch.zeros((sb, cw.H, 64, 64), dtype=torch.float32, device="cuda")
+        ks = torch.zeros((sb, cw.H, 64), dtype=torch.float32, device="cuda")
+
+        def stream_pass():
+            for b in range(nblk):
+                L = ropes[b].grid[0] * hw
+                x = blk[L]
+                for d in range(steps):
+                    commit = d == steps - 1
+                    hla.hla_linear_attn_chunked(x["q"], x["k"], x["v"], L, None, ropes[b], cw.eps, kv_in=kv,
+                                                ksum_in=ks, kv_out=kv if commit else None,
+                                                ksum_out=ks if commit else None, o=x["o"], ws=ws)
+
+        stream_pass()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            stream_pass()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        s_ms = float(np.mean(times))
+        s_bytes = steps * sb * cw.N * cw.H * 64 * 2 * 4  # per call: Q, K, V read + O written
+        out["legs"]["stream_720p60s_cfg_pair"] = {
+            "B": sb, "N": cw.N, "blocks": nblk, "steps_per_block": steps, "calls": nblk * steps, "ms": s_ms,
+            "tokens_per_s": steps * sb * cw.N / (s_ms * 1e-3), "hbm_gbs": s_bytes / (s_ms * 1e-3) / 1e9,
+            "hbm_frac": s_bytes / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": s_bytes}
+        log(f"[bench] streaming: {s_ms:.3f} ms for {nblk * steps} calls")
+        del blk, ws
+        torch.cuda.empty_cache()
+
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_heads} heads")
         out["cpu_baseline"] = cpu_baseline(args.cpu_heads)

@@ -19,31 +19,11 @@ import oracle
 import synth
 from softmax_attention_relu_amd import hla
 
+from gpu_common import TOL_BF16, TOL_F32, dev, host, normwise, say
+
 pytestmark = pytest.mark.gpu
 
-TOL_BF16 = 1e-2
-TOL_F32 = 1e-5
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-
-
-def say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
-
-
-def dev(x):
-    if x.dtype == np.uint16:
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
-    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
-
-
-def host(t):
-    return t.float().cpu().numpy().astype(np.float64)
-
-
-def normwise(got, ref):
-    den = np.abs(ref).max()
-    return float(np.abs(got - ref).max() / den) if den > 0 else float(np.abs(got).max())
 
 
 def tol(dtype):
