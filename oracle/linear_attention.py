@@ -118,3 +118,44 @@ def linear_attention_chunked(q, k, v, chunk_tokens: int, g=None, rope: Rope3D | 
     if rows is not None:
         out = out[:, np.asarray(rows)]
     return out, kv, k_sum
+
+
+def linear_attention_causal(q, k, v, g=None, rope: Rope3D | None = None, eps: float = 1e-6, kv_in=None,
+                            ksum_in=None, rows=None):
+    """Token-causal linear attention, fp64 (SANA-Video notes, section 3.4, causal equation).
+
+    Token i sees every token j <= i, itself included, on top of an optional
+    carried state:
+
+        KV_i   = KV_in   + sum_{j <= i} c_j^T v_j
+        ksum_i = ksum_in + sum_{j <= i} phi(k_j)
+        o_i    = (a_i KV_i) / (phi(q_i) . ksum_i + eps)     [then the gate]
+
+    Returns (out, kv_out, ksum_out), the state being the one after the last
+    token. ``rows`` selects the outputs returned (any order); the sums are
+    accumulated segment by segment between the requested rows, so memory
+    stays O(D^2) however long the sequence.
+    """
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    B, N, H, D = q.shape
+    q_relu, k_relu, q_rope, k_rope = _features(q, k, rope)
+    kv = np.zeros((B, H, D, D)) if kv_in is None else np.array(kv_in, dtype=np.float64)
+    k_sum = np.zeros((B, H, D)) if ksum_in is None else np.array(ksum_in, dtype=np.float64)
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    out = np.zeros((B, len(rows), H, D))
+    done = 0  # tokens already summed into kv, k_sum
+    for idx in np.argsort(rows, kind="stable"):
+        i = int(rows[idx])
+        if i + 1 > done:
+            kv = kv + np.einsum("bnhd,bnhe->bhde", k_rope[:, done:i + 1], v[:, done:i + 1])
+            k_sum = k_sum + k_relu[:, done:i + 1].sum(axis=1)
+            done = i + 1
+        num = np.einsum("bhd,bhde->bhe", q_rope[:, i], kv)
+        den = np.einsum("bhd,bhd->bh", q_relu[:, i], k_sum)
+        out[:, idx] = num / (den[..., None] + eps)
+    if done < N:
+        kv = kv + np.einsum("bnhd,bnhe->bhde", k_rope[:, done:], v[:, done:])
+        k_sum = k_sum + k_relu[:, done:].sum(axis=1)
+    if g is not None:
+        out = _sigmoid(g[:, rows]) * out
+    return out, kv, k_sum

@@ -40,6 +40,12 @@ MUTATIONS = [
      "        k_sum = k_sum + q_relu[:, start:stop].sum(axis=1)"),
     ("linear_attention.py", "        out[:, start:stop] = num / (den[..., None] + eps)\n    if g",
      "        out[:, start:stop] = num / (den[..., None] + eps)\n    if False"),
+    # token-causal: exclusive instead of inclusive prefix, RoPE on the denominator
+    ("linear_attention.py",
+     'kv = kv + np.einsum("bnhd,bnhe->bhde", k_rope[:, done:i + 1], v[:, done:i + 1])',
+     'kv = kv + np.einsum("bnhd,bnhe->bhde", k_rope[:, done:i], v[:, done:i])'),
+    ("linear_attention.py", 'den = np.einsum("bhd,bhd->bh", q_relu[:, i], k_sum)',
+     'den = np.einsum("bhd,bhd->bh", q_rope[:, i], k_sum)'),
     # anchor: missing scale, softmax over the wrong axis
     ("softmax_anchor.py", "logits = scale * (q[b, rr, h, :] @ kh.T)", "logits = (q[b, rr, h, :] @ kh.T)"),
     ("softmax_anchor.py", "p = p / p.sum(axis=1, keepdims=True)", "p = p / p.sum(axis=0, keepdims=True)"),
