@@ -192,9 +192,14 @@ def main() -> int:
                     ev["anchor"][1].record()
 
     if args.profile_pass:
-        log("[bench] profile pass: one step, one 720p/60s chunked call, then a 1 GiB copy (calibration)")
+        log("[bench] profile pass: one step, one token-causal call, one 720p/60s chunked call, "
+            "then a 1 GiB copy (calibration)")
         step()
         torch.cuda.synchronize()
+        if not args.no_legs:
+            cw0, cx0 = lin[0]
+            hla.hla_linear_attn_causal(cx0["q"], cx0["k"], cx0["v"], cx0["g"], cx0["rope"], cw0.eps)
+            torch.cuda.synchronize()
         if not args.no_legs:
             del lin, routes
             torch.cuda.empty_cache()
@@ -284,6 +289,35 @@ def main() -> int:
         },
     }
 
+    # ---------------- token-causal leg: the first 720p/5s linear layer's inputs, causal
+    if not args.no_legs:
+        cq = lin[0][1]
+        cws = torch.empty(hla.hla_linear_attn_causal_workspace(w0.B, w0.N, w0.H, w0.D), dtype=torch.uint8,
+                          device="cuda")
+        crope = hla.Rope3D(w0.grid, w0.bands, w0.base)
+        co = torch.empty_like(cq["q"])
+
+        def causal_call():
+            hla.hla_linear_attn_causal(cq["q"], cq["k"], cq["v"], cq["g"], crope, w0.eps, o=co, ws=cws)
+
+        causal_call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            causal_call()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        ca_ms = float(np.mean(times))
+        out.setdefault("legs", {})["causal_720p5s"] = {
+            "N": w0.N, "ms": ca_ms, "tokens_per_s": w0.B * w0.N / (ca_ms * 1e-3),
+            "hbm_gbs": lin_bytes / (ca_ms * 1e-3) / 1e9, "hbm_frac": lin_bytes / (ca_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": lin_bytes}
+        log(f"[bench] token-causal 720p/5s: {ca_ms:.3f} ms")
+        del cws, co
+
     # ---------------- block-causal 720p/60s leg
     if not args.no_legs:
         del lin, routes
@@ -314,10 +348,10 @@ def main() -> int:
             times.append(a.elapsed_time(b))
         c_ms = float(np.mean(times))
         c_bytes = cw.B * cw.N * cw.H * 64 * 2 * 4  # Q, K, V read + O written
-        out["legs"] = {"chunked_720p60s": {
+        out.setdefault("legs", {})["chunked_720p60s"] = {
             "N": cw.N, "chunk_tokens": cw.chunk_tokens, "ms": c_ms, "tokens_per_s": cw.B * cw.N / (c_ms * 1e-3),
             "hbm_gbs": c_bytes / (c_ms * 1e-3) / 1e9, "hbm_frac": c_bytes / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "algorithmic_bytes": c_bytes}}
+            "algorithmic_bytes": c_bytes}
         log(f"[bench] chunked: {c_ms:.3f} ms")
         del cx, ws
         torch.cuda.empty_cache()

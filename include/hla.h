@@ -9,6 +9,8 @@
  *                            optional sigmoid output gate.
  *   hla_linear_attn_chunked  block-causal variant that carries the cumulative
  *                            D x D state and key sum across chunks.
+ *   hla_linear_attn_causal   token-causal variant: every token sees itself and
+ *                            the tokens before it, plus a carried state.
  *   hla_softmax_anchor       gated non-causal softmax attention (the periodic
  *                            full-rank anchor layer).
  *   hla_attnres_route        block attention-residual (AttnRes) depth router.
@@ -29,7 +31,7 @@
  *   exception crosses this interface. The library holds no mutable global
  *   state, so calls from several host threads are safe.
  * - Aliasing: outputs must not overlap inputs, except kv_out == kv_in and
- *   ksum_out == ksum_in in hla_linear_attn_chunked.
+ *   ksum_out == ksum_in in hla_linear_attn_chunked and hla_linear_attn_causal.
  * - Numbers: HLA_BF16 tensors hold bfloat16 values, HLA_F32 tensors float.
  *   States, key sums, router queries and RoPE tables are always float.
  *   Arithmetic is float32 throughout; bf16 outputs are rounded to nearest
@@ -132,6 +134,28 @@ hla_status hla_linear_attn_chunked(hla_dtype dt, int B, int N, int H, int D, int
                                    const float *kv_in, const float *ksum_in,
                                    float *kv_out, float *ksum_out,
                                    void *o, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Token-causal linear attention (SANA-Video notes, section 3.4, the causal
+ * equation with the own term included): token i gets
+ *   o_i = (a_i KV_i) / (relu(q_i) . z_i + eps),  then the optional gate,
+ * with KV_i = KV_in + sum_{j <= i} c_j^T v_j and z_i = z_in + sum_{j <= i}
+ * relu(k_j) (a, c as in hla_linear_attn). It equals hla_linear_attn_chunked
+ * with chunk_tokens = 1, computed in 32-token steps on the matrix cores.
+ * kv_in/ksum_in (may both be NULL: zero state) and kv_out/ksum_out (may both
+ * be NULL: no commit; receive the state after the last token; may alias the
+ * inputs) as in hla_linear_attn_chunked. Other arguments as hla_linear_attn.
+ * Errors: as hla_linear_attn_chunked, plus UNSUPPORTED for dt != HLA_BF16 and
+ * for a rope whose band widths are not multiples of 8 or whose tables are not
+ * 16-byte aligned.
+ */
+size_t hla_linear_attn_causal_workspace(int B, int N, int H, int D);
+hla_status hla_linear_attn_causal(hla_dtype dt, int B, int N, int H, int D,
+                                  const void *q, const void *k, const void *v, const void *g,
+                                  const hla_rope3d *rope, float eps,
+                                  const float *kv_in, const float *ksum_in,
+                                  float *kv_out, float *ksum_out,
+                                  void *o, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Gated non-causal softmax attention, the anchor layer of the 3:1 hybrid

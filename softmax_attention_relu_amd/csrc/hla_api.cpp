@@ -125,6 +125,46 @@ hla_status hla_linear_attn_chunked(hla_dtype dt, int B, int N, int H, int D, int
                        ws_bytes, stream);
 }
 
+size_t hla_linear_attn_causal_workspace(int B, int N, int H, int D) {
+  if (!shape_ok(B, N, H) || D != kD) return 0;
+  return plan_linear_causal(B, N, H).total_bytes;
+}
+
+hla_status hla_linear_attn_causal(hla_dtype dt, int B, int N, int H, int D, const void *q, const void *k,
+                                  const void *v, const void *g, const hla_rope3d *rope, float eps, const float *kv_in,
+                                  const float *ksum_in, float *kv_out, float *ksum_out, void *o, void *ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o) return HLA_ERR_INVALID_ARG;
+  if (!shape_ok(B, N, H)) return HLA_ERR_INVALID_ARG;
+  if ((kv_in == nullptr) != (ksum_in == nullptr)) return HLA_ERR_INVALID_ARG;
+  if ((kv_out == nullptr) != (ksum_out == nullptr)) return HLA_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || isinf(eps)) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16 && dt != HLA_F32) return HLA_ERR_UNSUPPORTED;
+  if (D != kD) return HLA_ERR_UNSUPPORTED;
+  if (!rope_valid(rope, N, D)) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16) return HLA_ERR_UNSUPPORTED;
+  LinearArgs a;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.o = o;
+  a.rope = make_rope(rope);
+  if (a.rope.enabled && !a.rope.aligned) return HLA_ERR_UNSUPPORTED;
+  const LinearPlan plan = plan_linear_causal(B, N, H);
+  if (!ws || ws_bytes < plan.total_bytes) return HLA_ERR_WORKSPACE;
+  a.eps = eps;
+  a.kv_in = kv_in;
+  a.ksum_in = ksum_in;
+  a.kv_out = kv_out;
+  a.ksum_out = ksum_out;
+  a.ws = ws;
+  return launch_linear_causal(a, plan, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
+}
+
 size_t hla_softmax_anchor_workspace(int B, int N, int H, int D) {
   if (!shape_ok(B, N, H) || D != kD) return 0;
   return anchor_workspace_bytes(B, N, H);

@@ -48,6 +48,7 @@ struct LinearPlan {
   int apply_per_chunk;  // apply work-groups per (b, head group, chunk); part p takes steps p, p+A, ...
   int ngroups;          // head groups of 4 (one head per wave)
   size_t part_offset, prefix_offset, total_bytes;  // workspace layout (bytes)
+  size_t init_offset = 0;  // causal path: copy of the incoming state
 };
 
 LinearPlan plan_linear(int B, int N, int H, int chunk_tokens);
@@ -64,6 +65,11 @@ struct LinearArgs {
 };
 
 hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p, hipStream_t stream);
+
+// Token-causal path (bf16, band widths multiples of 8): ranges of whole
+// 32-token steps as the chunks of the state build and scan.
+LinearPlan plan_linear_causal(int B, int N, int H);
+hipError_t launch_linear_causal(const LinearArgs &a, const LinearPlan &p, hipStream_t stream);
 
 struct AnchorArgs {
   int B, N, H;

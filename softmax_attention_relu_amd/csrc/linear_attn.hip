@@ -430,6 +430,7 @@ struct ScanArgs {
   const float *kv_in, *ksum_in;
   float *kv_out, *ksum_out;
   float *prefix;  // [B*H][n_chunks][kStateFloats]
+  float *init;    // nullable: receives the incoming state (kv_in or zero) [B*H][kStateFloats]
 };
 
 __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
@@ -438,6 +439,9 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
   const int bh = blockIdx.y;
   float run = 0.f;
   if (a.kv_in) run = idx < kD * kD ? a.kv_in[(size_t)bh * kD * kD + idx] : a.ksum_in[(size_t)bh * kD + idx - kD * kD];
+  // a copy of the incoming state for readers that run after kv_out (which may
+  // alias kv_in) has been written
+  if (a.init) a.init[(size_t)bh * kStateFloats + idx] = run;
   const int nsl = a.n_chunks * a.slabs_per_chunk;
   const float *p = a.part + (size_t)bh * nsl * kStateFloats + idx;
   float *pre = a.prefix + (size_t)bh * a.n_chunks * kStateFloats + idx;
@@ -826,6 +830,328 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// ---------------------------------------------------------------------------
+// Token-causal apply (bf16). Token i sees the state of every token j <= i:
+//   o_i = (a_i (P + sum_{j<=i, j in range} c_j^T v_j)) /
+//         (phi(q_i) . (z + sum_{j<=i} phi(k_j)) + eps)
+// with (P, z) the state of all tokens before the range (exclusive prefix).
+// A wave owns one head of one token range and walks it in 32-token steps,
+// carrying the state S (fp32, in matrix-core accumulators) and the key sum z
+// (in LDS). Per step, with i the query and j the key within the step:
+//   O^T  = S^T a^T                      inter-step part (S as bf16 hi + lo)
+//   T^T  = C A^T, U^T = phi(K) phi(Q)^T  scores, rotated and plain
+//   O^T += V^T (T^T masked to j <= i)   intra-step part (T as bf16 hi + lo)
+//   den  = phi(q_i).z + sum_{j<=i} U^T[j][i] + eps
+//   S   += C^T V,  z += sum_j phi(k_j)   (after this step's outputs)
+// Dim order. Every product over dims uses the order the state accumulators
+// hold: lane half h supplies dims d0..d0+3 and d0+8..d0+11, d0 = 32kb + 16s +
+// 4h, for reduction step (kb, s). q and k are loaded in that order (8-byte
+// pieces), so S's accumulator entries 8s..8s+7 are directly the A operand of
+// the inter-step product. Key order. C^T and V^T go to LDS transposed with the
+// keys of each group of 16 permuted (bits 2 and 3 swapped), so that the masked
+// scores, read from their accumulators as the B operand of the P.V product,
+// match contiguous 16-byte reads of V^T; the state update reads C^T and V^T
+// with the same key order on both sides.
+constexpr int kCtRow = kApplySub + 8;  // bf16 per transposed row (32 keys + pad)
+
+struct CausalArgs {
+  const uint16_t *q, *k, *v, *g;
+  uint16_t *o;
+  int N, H, L, n_chunks, ngroups;
+  RopeArgs rope;
+  float eps;
+  const float *prefix;  // inclusive prefix per range: [B*H][n_chunks][kStateFloats]
+  const float *init;    // state before the first range: [B*H][kStateFloats]
+};
+
+__device__ __forceinline__ int key_perm(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// (cos, sin) of the two pairs of the 4-dim run starting at dim d (d % 4 == 0)
+__device__ __forceinline__ f32x4_t rope_run(const RopeArgs &r, const TokenPos &tp, int d) {
+  const float *col;
+  int stride;
+  uint32_t pos;
+  if (d < r.d_t) {
+    col = r.cs_t + d;
+    stride = r.d_t;
+    pos = tp.t;
+  } else if (d < r.d_t + r.d_h) {
+    col = r.cs_h + (d - r.d_t);
+    stride = r.d_h;
+    pos = tp.y;
+  } else {
+    col = r.cs_w + (d - r.d_t - r.d_h);
+    stride = r.d_w;
+    pos = tp.x;
+  }
+  return *reinterpret_cast<const f32x4_t *>(col + (size_t)pos * stride);
+}
+
+template <bool kRope, bool kGate>
+__global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
+  __shared__ __align__(16) uint16_t ct_all[kHeadsPerWG][kD * kCtRow];
+  __shared__ __align__(16) uint16_t vt_all[kHeadsPerWG][kD * kCtRow];
+  __shared__ __align__(16) float z_all[kHeadsPerWG][kD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, tl = lane & 31;
+  const int hgroup = blockIdx.x % a.ngroups;
+  const int rng = blockIdx.x / a.ngroups;
+  const int h = kHeadsPerWG * hgroup + wave;
+  if (h >= a.H) return;  // no work-group barrier in this kernel
+  const int b = blockIdx.y;
+  const int bh = b * a.H + h;
+  const int lo = rng * a.L;
+  const int hi_r = min(a.N, lo + a.L);
+  if (lo >= hi_r) return;
+  uint16_t *ct = ct_all[wave];
+  uint16_t *vt = vt_all[wave];
+  float *zs = z_all[wave];
+
+  // state before the range: S[d][e] in accumulator layout (rows d, column e)
+  const float *P = rng > 0 ? a.prefix + ((size_t)bh * a.n_chunks + rng - 1) * kStateFloats
+                           : a.init + (size_t)bh * kStateFloats;
+  const float *Pz = P + kD * kD;
+  f32x16_t sacc[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sacc[kb][nb][4 * i + j] = P[(32 * kb + 8 * i + 4 * half + j) * kD + 32 * nb + tl];
+  zs[lane] = Pz[lane];
+  wave_lds_fence();
+
+  const size_t tok_stride = (size_t)a.H * kD;
+  const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD;
+  const int kp_self = key_perm(tl);
+
+  for (int sub = lo; sub < hi_r; sub += kApplySub) {
+    const int hi = min(hi_r, sub + kApplySub);
+    const int n = sub + tl;
+    const bool valid = n < hi;
+    const size_t row = head_base + (size_t)min(n, hi - 1) * tok_stride;
+
+    // v as 16-byte pieces; q and k are read per reduction step below, in the
+    // state's dim order (8-byte pieces)
+    uint4 vp[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) vp[s] = *reinterpret_cast<const uint4 *>(a.v + row + 16 * s + 8 * half);
+    TokenPos tp;
+    if constexpr (kRope) tp = token_pos(a.rope, (uint32_t)min(n, hi - 1));
+    if (!valid) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) vp[s] = make_uint4(0, 0, 0, 0);
+    }
+
+    // V^T to LDS: row = dim, column = permuted key
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t w[4] = {vp[s].x, vp[s].y, vp[s].z, vp[s].w};
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        vt[(16 * s + 8 * half + t) * kCtRow + kp_self] = (uint16_t)((t & 1) ? (w[t >> 1] >> 16) : (w[t >> 1] & 0xFFFFu));
+    }
+
+    f32x16_t tacc, uacc, oacc[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      tacc[i] = 0.f;
+      uacc[i] = 0.f;
+      oacc[0][i] = 0.f;
+      oacc[1][i] = 0.f;
+    }
+    float den_in = 0.f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kb = st >> 1, s2 = st & 1;
+      const int d0 = 32 * kb + 16 * s2 + 4 * half;
+      float fq[8], fk[8];
+      uint2 q0 = *reinterpret_cast<const uint2 *>(a.q + row + d0);
+      uint2 q1 = *reinterpret_cast<const uint2 *>(a.q + row + d0 + 8);
+      uint2 k0 = *reinterpret_cast<const uint2 *>(a.k + row + d0);
+      uint2 k1 = *reinterpret_cast<const uint2 *>(a.k + row + d0 + 8);
+      if (!valid) q0 = q1 = k0 = k1 = make_uint2(0, 0);
+      const uint32_t qw[4] = {q0.x, q0.y, q1.x, q1.y};
+      const uint32_t kw[4] = {k0.x, k0.y, k1.x, k1.y};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        fq[2 * u] = fmaxf(bf16_lo(qw[u]), 0.f);
+        fq[2 * u + 1] = fmaxf(bf16_hi(qw[u]), 0.f);
+        fk[2 * u] = fmaxf(bf16_lo(kw[u]), 0.f);
+        fk[2 * u + 1] = fmaxf(bf16_hi(kw[u]), 0.f);
+      }
+      // denominator against the key sum before this step
+      {
+        const f32x4_t z0 = *reinterpret_cast<const f32x4_t *>(zs + d0);
+        const f32x4_t z1 = *reinterpret_cast<const f32x4_t *>(zs + d0 + 8);
+        den_in += fq[0] * z0.x + fq[1] * z0.y + fq[2] * z0.z + fq[3] * z0.w;
+        den_in += fq[4] * z1.x + fq[5] * z1.y + fq[6] * z1.z + fq[7] * z1.w;
+      }
+      // this step's key sum for these dims: sum over the 32 tokens (lane bits 0..4)
+      {
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = fk[t];
+        // lane bit 4: pairs (t, t + 4)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[t]), __float_as_uint(v[t + 4]), false,
+                                                          false);
+          v[t] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+        const bool b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {  // lane bit 3: partner by a rotation of 8 inside the row
+          const float keep = b3 ? v[t + 2] : v[t];
+          const float give = b3 ? v[t] : v[t + 2];
+          v[t] = keep + dpp_f32<0x128>(give);
+        }
+        {  // lane bit 2: row half mirror
+          const float keep = b2 ? v[1] : v[0];
+          const float give = b2 ? v[0] : v[1];
+          v[0] = keep + dpp_f32<0x141>(give);
+        }
+        v[0] += dpp_f32<0x4E>(v[0]);  // lane bit 1
+        v[0] += dpp_f32<0xB1>(v[0]);  // lane bit 0
+        // v[0] is the sum for value 4*bit4 + 2*bit3 + bit2 of this half
+        const int t = 4 * ((lane >> 4) & 1) + 2 * b3 + b2;
+        if ((lane & 3) == 0) zs[(t < 4 ? d0 + t : d0 + 4 + t)] += v[0];
+      }
+      float qa[8], kc[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        qa[t] = fq[t];
+        kc[t] = fk[t];
+      }
+      if constexpr (kRope) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x4_t c4 = rope_run(a.rope, tp, d0 + 8 * u);
+          rotate(qa[4 * u], qa[4 * u + 1], f32x2_t{c4.x, c4.y});
+          rotate(qa[4 * u + 2], qa[4 * u + 3], f32x2_t{c4.z, c4.w});
+          rotate(kc[4 * u], kc[4 * u + 1], f32x2_t{c4.x, c4.y});
+          rotate(kc[4 * u + 2], kc[4 * u + 3], f32x2_t{c4.z, c4.w});
+        }
+      }
+      const uint32_t aw[4] = {pack_bf16(qa[0], qa[1]), pack_bf16(qa[2], qa[3]), pack_bf16(qa[4], qa[5]),
+                              pack_bf16(qa[6], qa[7])};
+      const uint32_t cw[4] = {pack_bf16(kc[0], kc[1]), pack_bf16(kc[2], kc[3]), pack_bf16(kc[4], kc[5]),
+                              pack_bf16(kc[6], kc[7])};
+      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+      const bf16x8_t C = __builtin_bit_cast(bf16x8_t, make_uint4(cw[0], cw[1], cw[2], cw[3]));
+      const bf16x8_t Qu = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16(fq[0], fq[1]), pack_bf16(fq[2], fq[3]),
+                                                                  pack_bf16(fq[4], fq[5]), pack_bf16(fq[6], fq[7])));
+      const bf16x8_t Ku = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16(fk[0], fk[1]), pack_bf16(fk[2], fk[3]),
+                                                                  pack_bf16(fk[4], fk[5]), pack_bf16(fk[6], fk[7])));
+      // C^T to LDS (row = dim, column = permuted key)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int d = t < 4 ? d0 + t : d0 + 4 + t;
+        ct[d * kCtRow + kp_self] = (uint16_t)((t & 1) ? (cw[t >> 1] >> 16) : (cw[t >> 1] & 0xFFFFu));
+      }
+      tacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(C, A, tacc, 0, 0, 0);
+      uacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ku, Qu, uacc, 0, 0, 0);
+      // inter-step: O^T += S^T a^T, S entries 8*s2 .. 8*s2+7 of block (kb, mb) as hi + lo
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float x0 = sacc[kb][mb][8 * s2 + 2 * u], x1 = sacc[kb][mb][8 * s2 + 2 * u + 1];
+          wh[u] = pack_bf16(x0, x1);
+          wl[u] = pack_bf16(x0 - bf16_lo(wh[u]), x1 - bf16_hi(wh[u]));
+        }
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, make_uint4(wh[0], wh[1], wh[2], wh[3])), A, oacc[mb], 0, 0, 0);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, make_uint4(wl[0], wl[1], wl[2], wl[3])), A, oacc[mb], 0, 0, 0);
+      }
+    }
+    wave_lds_fence();  // C^T, V^T and z written
+
+    // causal mask: the lane holds keys 8i + 4*half + j of query tl
+    float den = den_in + __shfl_xor(den_in, 32);
+    float dsum = 0.f;
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool keep = 8 * i + 4 * half + j <= tl;
+        p[4 * i + j] = keep ? tacc[4 * i + j] : 0.f;
+        dsum += keep ? uacc[4 * i + j] : 0.f;
+      }
+    den += dsum + __shfl_xor(dsum, 32) + a.eps;
+    // intra-step: O^T += V^T P^T, P as hi + lo
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float x0 = p[8 * u + 2 * w], x1 = p[8 * u + 2 * w + 1];
+        wh[w] = pack_bf16(x0, x1);
+        wl[w] = pack_bf16(x0 - bf16_lo(wh[w]), x1 - bf16_hi(wh[w]));
+      }
+      const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+      const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, make_uint4(wl[0], wl[1], wl[2], wl[3]));
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8_t va = *reinterpret_cast<const bf16x8_t *>(vt + (32 * mb + tl) * kCtRow + 16 * u + 8 * half);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, ph, oacc[mb], 0, 0, 0);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pl, oacc[mb], 0, 0, 0);
+      }
+    }
+    // state update: S += C^T V over the step's keys (same key order on both sides)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8_t cta[2], vtb[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        cta[x] = *reinterpret_cast<const bf16x8_t *>(ct + (32 * x + tl) * kCtRow + 16 * s + 8 * half);
+        vtb[x] = *reinterpret_cast<const bf16x8_t *>(vt + (32 * x + tl) * kCtRow + 16 * s + 8 * half);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          sacc[kb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cta[kb], vtb[nb], sacc[kb][nb], 0, 0, 0);
+    }
+
+    // normalise, gate, store: lane holds dims 32*mb + 8i + 4*half + j of token n
+    const float inv = 1.f / den;
+    if (valid) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const size_t off = row + 32 * mb + 8 * i + 4 * half;
+          float y[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = oacc[mb][4 * i + j] * inv;
+          if constexpr (kGate) {
+            const uint2 gw = *reinterpret_cast<const uint2 *>(a.g + off);
+            y[0] *= sigmoid_fast(bf16_lo(gw.x));
+            y[1] *= sigmoid_fast(bf16_hi(gw.x));
+            y[2] *= sigmoid_fast(bf16_lo(gw.y));
+            y[3] *= sigmoid_fast(bf16_hi(gw.y));
+          }
+          *reinterpret_cast<uint2 *>(a.o + off) = make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
+        }
+    }
+    wave_lds_fence();  // the next step's LDS writes come after these reads
+  }
+}
+
 template <bool kBF16, bool kRope, bool kAligned>
 hipError_t launch_build(dim3 grid, const BuildArgs &ba, hipStream_t stream) {
   const size_t lds = 4 * (size_t)(kBF16 ? kWaveLds16 : kWaveLds32);
@@ -890,7 +1216,10 @@ LinearPlan plan_linear(int B, int N, int H, int chunk_tokens) {
   return p;
 }
 
-hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p, hipStream_t stream) {
+// State build and scan shared by the bidirectional, chunked and causal paths;
+// *prefix_out receives the inclusive prefix per chunk.
+static hipError_t build_and_scan(hla_dtype dt, const LinearArgs &a, const LinearPlan &p, hipStream_t stream,
+                                 float **prefix_out, float *init = nullptr) {
   const int heads = a.B * a.H;
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(a.ws) + p.part_offset);
   float *prefix = reinterpret_cast<float *>(reinterpret_cast<char *>(a.ws) + p.prefix_offset);
@@ -924,10 +1253,20 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
   sa.kv_out = a.kv_out;
   sa.ksum_out = a.ksum_out;
   sa.prefix = prefix;
+  sa.init = init;
   hipLaunchKernelGGL(la_scan_kernel, dim3((kStateFloats + 255) / 256, heads), dim3(256), 0, stream, sa);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  *prefix_out = prefix;
+  return hipSuccess;
+}
 
+hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p, hipStream_t stream) {
+  float *prefix = nullptr;
+  {
+    const hipError_t e = build_and_scan(dt, a, p, stream, &prefix);
+    if (e != hipSuccess) return e;
+  }
   ApplyArgs aa;
   aa.q = a.q;
   aa.g = a.g;
@@ -961,6 +1300,57 @@ hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p,
       launch_apply_bf16<kRopeGlobal>(gate, agrid, aa, stream);
   } else
     hipLaunchKernelGGL(la_apply_f32_kernel, agrid, dim3(256), 0, stream, aa);
+  return hipGetLastError();
+}
+
+LinearPlan plan_linear_causal(int B, int N, int H) {
+  // one work-group per (b, head group, range), about 512 in all; ranges are
+  // whole 32-token steps and carry their state sequentially
+  const long long groups = (long long)B * ((H + kHeadsPerWG - 1) / kHeadsPerWG);
+  const long long ranges = std::max(1LL, 512 / groups);
+  long long len = ((long long)N + ranges - 1) / ranges;
+  len = std::max<long long>(kApplySub, (len + kApplySub - 1) / kApplySub * kApplySub);
+  LinearPlan p = plan_linear(B, N, H, (int)std::min<long long>(len, N));
+  p.init_offset = p.total_bytes;  // copy of the incoming state
+  p.total_bytes += align256((size_t)B * H * kStateFloats * sizeof(float));
+  return p;
+}
+
+hipError_t launch_linear_causal(const LinearArgs &a, const LinearPlan &p, hipStream_t stream) {
+  float *prefix = nullptr;
+  float *init = reinterpret_cast<float *>(reinterpret_cast<char *>(a.ws) + p.init_offset);
+  {
+    const hipError_t e = build_and_scan(HLA_BF16, a, p, stream, &prefix, init);
+    if (e != hipSuccess) return e;
+  }
+  CausalArgs ca;
+  ca.q = reinterpret_cast<const uint16_t *>(a.q);
+  ca.k = reinterpret_cast<const uint16_t *>(a.k);
+  ca.v = reinterpret_cast<const uint16_t *>(a.v);
+  ca.g = reinterpret_cast<const uint16_t *>(a.g);
+  ca.o = reinterpret_cast<uint16_t *>(a.o);
+  ca.N = a.N;
+  ca.H = a.H;
+  ca.L = p.chunk_len;
+  ca.n_chunks = p.n_chunks;
+  ca.ngroups = p.ngroups;
+  ca.rope = a.rope;
+  ca.eps = a.eps;
+  ca.prefix = prefix;
+  ca.init = init;
+  const dim3 grid(p.n_chunks * p.ngroups, a.B);
+  const bool gate = a.g != nullptr;
+  if (a.rope.enabled) {
+    if (gate)
+      hipLaunchKernelGGL((la_causal_kernel<true, true>), grid, dim3(256), 0, stream, ca);
+    else
+      hipLaunchKernelGGL((la_causal_kernel<true, false>), grid, dim3(256), 0, stream, ca);
+  } else {
+    if (gate)
+      hipLaunchKernelGGL((la_causal_kernel<false, true>), grid, dim3(256), 0, stream, ca);
+    else
+      hipLaunchKernelGGL((la_causal_kernel<false, false>), grid, dim3(256), 0, stream, ca);
+  }
   return hipGetLastError();
 }
 

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     const size_t row = (size_t)tok * a.C;
 
     // this lane's share of sum v^2 and u.v for every source
-    typename E::Chunk held[kKeep][CHL];
+    typename E::Chunk held[kKeep > 0 ? kKeep : 1][CHL];
     float part[2 * SMAX];
 #pragma unroll
     for (int i = 0; i < SMAX; ++i) {

@@ -29,6 +29,8 @@ EXPORTS = (
     "hla_linear_attn",
     "hla_linear_attn_chunked_workspace",
     "hla_linear_attn_chunked",
+    "hla_linear_attn_causal_workspace",
+    "hla_linear_attn_causal",
     "hla_softmax_anchor_workspace",
     "hla_softmax_anchor",
     "hla_attnres_route",
@@ -73,6 +75,12 @@ def lib() -> ctypes.CDLL:
                                               c_void_p, POINTER(hla_rope3d), c_float, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.hla_linear_attn_chunked.restype = c_int
+        L.hla_linear_attn_causal_workspace.argtypes = [c_int, c_int, c_int, c_int]
+        L.hla_linear_attn_causal_workspace.restype = c_size_t
+        L.hla_linear_attn_causal.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, POINTER(hla_rope3d), c_float, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.hla_linear_attn_causal.restype = c_int
         L.hla_softmax_anchor_workspace.argtypes = [c_int, c_int, c_int, c_int]
         L.hla_softmax_anchor_workspace.restype = c_size_t
         L.hla_softmax_anchor.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -221,6 +229,25 @@ def hla_linear_attn_chunked(q, k, v, chunk_tokens: int, g=None, rope: Rope3D | N
                                        _ptr(g), _rope_ptr(rope), float(eps), _ptr(kv_in), _ptr(ksum_in),
                                        _ptr(kv_out), _ptr(ksum_out), _ptr(o), _ptr(ws), nbytes, _stream(stream))
     _check(st, "hla_linear_attn_chunked")
+    return o
+
+
+def hla_linear_attn_causal_workspace(B: int, N: int, H: int, D: int) -> int:
+    return int(lib().hla_linear_attn_causal_workspace(B, N, H, D))
+
+
+def hla_linear_attn_causal(q, k, v, g=None, rope: Rope3D | None = None, eps: float = 1e-6, kv_in=None, ksum_in=None,
+                           kv_out=None, ksum_out=None, o=None, ws=None, stream=None):
+    """Token-causal linear attention (bf16) with optional carried state; returns o."""
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    if o is None:
+        o = torch.empty_like(q)
+    ws, nbytes = _workspace(hla_linear_attn_causal_workspace(B, N, H, D), q.device, ws)
+    st = lib().hla_linear_attn_causal(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                      _rope_ptr(rope), float(eps), _ptr(kv_in), _ptr(ksum_in), _ptr(kv_out),
+                                      _ptr(ksum_out), _ptr(o), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_linear_attn_causal")
     return o
 
 

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     assert sorted(hla.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -129,6 +129,23 @@ def test_chunked_validation(L):
     assert call(kv_in=FAKE) == E.HLA_ERR_INVALID_ARG  # ksum_in missing
     assert call(ks_out=FAKE) == E.HLA_ERR_INVALID_ARG  # kv_out missing
     assert call(ws_bytes=16) == E.HLA_ERR_WORKSPACE
+
+
+def test_causal_validation(L):
+    E = hla
+
+    def call(dt=0, rope=None, kv_in=None, ks_in=None, kv_out=None, ks_out=None, ws_bytes=1 << 40, q=FAKE):
+        return L.hla_linear_attn_causal(dt, 1, 8, 1, 64, q, FAKE, FAKE, None, ctypes.byref(rope) if rope else None,
+                                        1e-6, kv_in, ks_in, kv_out, ks_out, FAKE, FAKE, ws_bytes, None)
+
+    assert call(q=None) == E.HLA_ERR_INVALID_ARG
+    assert call(kv_in=FAKE) == E.HLA_ERR_INVALID_ARG  # ksum_in missing
+    assert call(ks_out=FAKE) == E.HLA_ERR_INVALID_ARG  # kv_out missing
+    assert call(dt=1) == E.HLA_ERR_UNSUPPORTED  # bf16 only
+    assert call(rope=_rope((2, 2, 2), (18, 22, 24))) == E.HLA_ERR_UNSUPPORTED  # band widths not multiples of 8
+    assert call(ws_bytes=16) == E.HLA_ERR_WORKSPACE
+    assert hla.hla_linear_attn_causal_workspace(1, 75600, 32, 64) > 0
+    assert hla.hla_linear_attn_causal_workspace(1, 75600, 32, 48) == 0
 
 
 def test_anchor_validation(L):
