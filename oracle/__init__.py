@@ -15,6 +15,8 @@ pages' order of operations:
                      notes, section 3.2, equation and pseudocode), with the
                      optional sigmoid output gate (the SANA-Video 2.0 abstract
                      describes the linear layers as gated).
+* ``linear_attention_backward`` -- gradients of the bidirectional (gated)
+                     variant, derived by hand from the definition.
 * ``linear_attention_causal`` -- token-causal variant (SANA-Video notes,
                      section 3.4, causal equation), with a carried state.
 * ``linear_attention_chunked`` -- block-causal variant with the carried
@@ -32,7 +34,8 @@ RoPE pairing and frequency convention (the pages do not define
 ``apply_3d_rope``); it is pinned only to the reading stated in ``rope3d``.
 """
 from .rope3d import Rope3D, rope3d_angles, rope3d_rotate
-from .linear_attention import linear_attention, linear_attention_causal, linear_attention_chunked
+from .linear_attention import (linear_attention, linear_attention_backward, linear_attention_causal,
+                               linear_attention_chunked)
 from .softmax_anchor import softmax_anchor
 from .attnres_router import attnres_route
 
@@ -41,6 +44,7 @@ __all__ = [
     "rope3d_angles",
     "rope3d_rotate",
     "linear_attention",
+    "linear_attention_backward",
     "linear_attention_causal",
     "linear_attention_chunked",
     "softmax_anchor",

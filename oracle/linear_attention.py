@@ -159,3 +159,49 @@ def linear_attention_causal(q, k, v, g=None, rope: Rope3D | None = None, eps: fl
     if g is not None:
         out = _sigmoid(g[:, rows]) * out
     return out, kv, k_sum
+
+
+def linear_attention_backward(q, k, v, do, g=None, rope: Rope3D | None = None, eps: float = 1e-6):
+    """Gradients of the bidirectional (gated) linear attention, fp64.
+
+    Differentiates the definition at the top of this module by hand. With
+    s_i = sigmoid(g_i) (1 without a gate), y_i = num_i / den_i and the upstream
+    gradient dO:
+
+        dG_i    = dO_i * y_i * s_i * (1 - s_i)
+        dY_i    = dO_i * s_i
+        dnum_i  = dY_i / den_i,        dden_i = -(dY_i . y_i) / den_i
+        da_i    = KV dnum_i,           dKV    = sum_i a_i^T dnum_i
+        dphiq_i = R_i^T da_i + dden_i ksum,   dksum = sum_i dden_i phi(q_i)
+        dc_j    = dKV v_j,             dv_j   = dKV^T c_j
+        dphik_j = R_j^T dc_j + dksum
+        dq = dphiq * [q > 0],          dk = dphik * [k > 0]
+
+    (R_i is the rotation of token i, so R_i^T undoes it; ReLU's derivative is
+    taken as 0 at 0.) Returns (dq, dk, dv, dg); dg is None without a gate.
+    """
+    q, k, v, do, g = _f64(q), _f64(k), _f64(v), _f64(do), _f64(g)
+    q_relu, k_relu, q_rope, k_rope = _features(q, k, rope)
+    kv = np.einsum("bnhd,bnhe->bhde", k_rope, v)
+    k_sum = k_relu.sum(axis=1)
+    num = np.einsum("bnhd,bhde->bnhe", q_rope, kv)
+    den = np.einsum("bnhd,bhd->bnh", q_relu, k_sum)[..., None] + eps
+    y = num / den
+    s = np.ones_like(y) if g is None else _sigmoid(g)
+    dg = None if g is None else do * y * s * (1.0 - s)
+    dy = do * s
+    dnum = dy / den
+    dden = -np.sum(dy * y, axis=-1, keepdims=True) / den
+    da = np.einsum("bhde,bnhe->bnhd", kv, dnum)
+    dkv = np.einsum("bnhd,bnhe->bhde", q_rope, dnum)
+    dk_sum = np.einsum("bnh,bnhd->bhd", dden[..., 0], q_relu)
+    dc = np.einsum("bhde,bnhe->bnhd", dkv, v)
+    dv = np.einsum("bhde,bnhd->bnhe", dkv, k_rope)
+    if rope is not None:
+        theta = rope3d_angles(rope)
+        da, dc = rope3d_rotate(da, -theta), rope3d_rotate(dc, -theta)
+    dphiq = da + dden * k_sum[:, None]
+    dphik = dc + dk_sum[:, None]
+    dq = dphiq * (q > 0)
+    dk = dphik * (k > 0)
+    return dq, dk, dv, dg

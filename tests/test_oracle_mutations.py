@@ -46,6 +46,12 @@ MUTATIONS = [
      'kv = kv + np.einsum("bnhd,bnhe->bhde", k_rope[:, done:i], v[:, done:i])'),
     ("linear_attention.py", 'den = np.einsum("bhd,bhd->bh", q_relu[:, i], k_sum)',
      'den = np.einsum("bhd,bhd->bh", q_rope[:, i], k_sum)'),
+    # backward: no inverse rotation, gate derivative factor, denominator sign, key-sum gradient
+    ("linear_attention.py", "da, dc = rope3d_rotate(da, -theta), rope3d_rotate(dc, -theta)", "da, dc = da, dc"),
+    ("linear_attention.py", "dg = None if g is None else do * y * s * (1.0 - s)", "dg = None if g is None else do * y * s"),
+    ("linear_attention.py", "dden = -np.sum(dy * y, axis=-1, keepdims=True) / den",
+     "dden = np.sum(dy * y, axis=-1, keepdims=True) / den"),
+    ("linear_attention.py", "dphik = dc + dk_sum[:, None]", "dphik = dc"),
     # anchor: missing scale, softmax over the wrong axis
     ("softmax_anchor.py", "logits = scale * (q[b, rr, h, :] @ kh.T)", "logits = (q[b, rr, h, :] @ kh.T)"),
     ("softmax_anchor.py", "p = p / p.sum(axis=1, keepdims=True)", "p = p / p.sum(axis=0, keepdims=True)"),
