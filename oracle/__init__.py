@@ -17,6 +17,8 @@ pages' order of operations:
                      describes the linear layers as gated).
 * ``linear_attention_backward`` -- gradients of the bidirectional (gated)
                      variant, derived by hand from the definition.
+* ``linear_attention_chunked_backward`` -- gradients of the block-causal
+                     variant, including those of the carried and returned cache.
 * ``linear_attention_causal`` -- token-causal variant (SANA-Video notes,
                      section 3.4, causal equation), with a carried state.
 * ``linear_attention_chunked`` -- block-causal variant with the carried
@@ -35,7 +37,7 @@ RoPE pairing and frequency convention (the pages do not define
 """
 from .rope3d import Rope3D, rope3d_angles, rope3d_rotate
 from .linear_attention import (linear_attention, linear_attention_backward, linear_attention_causal,
-                               linear_attention_chunked)
+                               linear_attention_chunked, linear_attention_chunked_backward)
 from .softmax_anchor import softmax_anchor
 from .attnres_router import attnres_route
 
@@ -47,6 +49,7 @@ __all__ = [
     "linear_attention_backward",
     "linear_attention_causal",
     "linear_attention_chunked",
+    "linear_attention_chunked_backward",
     "softmax_anchor",
     "attnres_route",
 ]

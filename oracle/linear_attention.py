@@ -205,3 +205,78 @@ def linear_attention_backward(q, k, v, do, g=None, rope: Rope3D | None = None, e
     dq = dphiq * (q > 0)
     dk = dphik * (k > 0)
     return dq, dk, dv, dg
+
+
+def linear_attention_chunked_backward(q, k, v, do, chunk_tokens: int, g=None, rope: Rope3D | None = None,
+                                      eps: float = 1e-6, kv_in=None, ksum_in=None, dkv_out=None, dksum_out=None):
+    """Gradients of the block-causal variant (``linear_attention_chunked``), fp64.
+
+    The loss is sum(dO * o) + sum(dKV_out * KV_out) + sum(dksum_out * ksum_out),
+    so the gradients reaching the returned cache are inputs too (zero when not
+    given). Chunk c's queries read the cache KV_c, ksum_c, which holds the
+    carried state and every chunk up to c. Per chunk, with the notation of
+    ``linear_attention_backward``:
+
+        dKV_c   = sum_{i in c} a_i^T dnum_i,      dksum_c = sum_{i in c} dden_i phi(q_i)
+        dphiq_i = R_i^T (KV_c dnum_i) + dden_i ksum_c
+
+    A key of chunk c is summed into the caches of chunks c, c+1, ... and into
+    the returned cache, so it sees the suffix sums
+
+        GKV_c = dKV_out + sum_{c' >= c} dKV_c',   Gz_c = dksum_out + sum_{c' >= c} dksum_c'
+        dphik_j = R_j^T (GKV_c v_j) + Gz_c,       dv_j = GKV_c^T c_j
+
+    and the carried state gets GKV_0, Gz_0. Returns
+    (dq, dk, dv, dg, dkv_in, dksum_in); dg is None without a gate.
+    """
+    if chunk_tokens <= 0:
+        raise ValueError("chunk_tokens must be positive")
+    q, k, v, do, g = _f64(q), _f64(k), _f64(v), _f64(do), _f64(g)
+    B, N, H, D = q.shape
+    q_relu, k_relu, q_rope, k_rope = _features(q, k, rope)
+    chunks = [slice(start, min(N, start + chunk_tokens)) for start in range(0, N, chunk_tokens)]
+    s = np.ones_like(q) if g is None else _sigmoid(g)
+    dg = None if g is None else np.zeros((B, N, H, D))
+
+    # query side, chunk by chunk against the cache that includes the chunk
+    kv = np.zeros((B, H, D, D)) if kv_in is None else np.array(kv_in, dtype=np.float64)
+    k_sum = np.zeros((B, H, D)) if ksum_in is None else np.array(ksum_in, dtype=np.float64)
+    da = np.zeros((B, N, H, D))        # KV_c dnum_i, still rotated
+    dz_term = np.zeros((B, N, H, D))   # dden_i ksum_c
+    dkv_chunk, dks_chunk = [], []
+    for sl in chunks:
+        kv = kv + np.einsum("bnhd,bnhe->bhde", k_rope[:, sl], v[:, sl])
+        k_sum = k_sum + k_relu[:, sl].sum(axis=1)
+        num = np.einsum("bnhd,bhde->bnhe", q_rope[:, sl], kv)
+        den = np.einsum("bnhd,bhd->bnh", q_relu[:, sl], k_sum)[..., None] + eps
+        y = num / den
+        if g is not None:
+            dg[:, sl] = do[:, sl] * y * s[:, sl] * (1.0 - s[:, sl])
+        dy = do[:, sl] * s[:, sl]
+        dnum = dy / den
+        dden = -np.sum(dy * y, axis=-1, keepdims=True) / den
+        da[:, sl] = np.einsum("bhde,bnhe->bnhd", kv, dnum)
+        dz_term[:, sl] = dden * k_sum[:, None]
+        dkv_chunk.append(np.einsum("bnhd,bnhe->bhde", q_rope[:, sl], dnum))
+        dks_chunk.append(np.einsum("bnh,bnhd->bhd", dden[..., 0], q_relu[:, sl]))
+
+    # key side: suffix sums over chunks, from the last chunk back
+    gkv = np.zeros((B, H, D, D)) if dkv_out is None else np.array(dkv_out, dtype=np.float64)
+    gz = np.zeros((B, H, D)) if dksum_out is None else np.array(dksum_out, dtype=np.float64)
+    dc = np.zeros((B, N, H, D))
+    dz_key = np.zeros((B, N, H, D))
+    dv = np.zeros((B, N, H, D))
+    for ci in range(len(chunks) - 1, -1, -1):
+        sl = chunks[ci]
+        gkv = gkv + dkv_chunk[ci]
+        gz = gz + dks_chunk[ci]
+        dc[:, sl] = np.einsum("bhde,bnhe->bnhd", gkv, v[:, sl])
+        dv[:, sl] = np.einsum("bhde,bnhd->bnhe", gkv, k_rope[:, sl])
+        dz_key[:, sl] = gz[:, None]
+
+    if rope is not None:
+        theta = rope3d_angles(rope)
+        da, dc = rope3d_rotate(da, -theta), rope3d_rotate(dc, -theta)
+    dq = (da + dz_term) * (q > 0)
+    dk = (dc + dz_key) * (k > 0)
+    return dq, dk, dv, dg, gkv, gz

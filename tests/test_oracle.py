@@ -439,6 +439,103 @@ def test_backward_matches_finite_differences():
             assert abs((up - dn) / (2 * h) - grad[idx]) <= 1e-5 * (1.0 + abs(grad[idx])), (which, idx)
 
 
+def _torch_chunked_forward(q, k, v, g, kv_in, ks_in, L, grid, bands, base, eps):
+    """Block-causal forward in its quadratic masked form (token j reaches token i when
+    chunk(j) <= chunk(i)), plus the carried state; returns (out, kv_out, ksum_out)."""
+    B, N, H, D = q.shape
+    fq, fk = torch.relu(q), torch.relu(k)
+    if grid is None:
+        a, c = fq, fk
+    else:
+        ang = torch.tensor([[_angle(n, p, grid, bands, base) for p in range(D // 2)] for n in range(N)],
+                           dtype=torch.float64)
+        cos, sin = torch.cos(ang)[None, :, None, :], torch.sin(ang)[None, :, None, :]
+
+        def rot(x):
+            ev, od = x[..., 0::2], x[..., 1::2]
+            return torch.stack([ev * cos - od * sin, ev * sin + od * cos], dim=-1).reshape(x.shape)
+
+        a, c = rot(fq), rot(fk)
+    blk = torch.arange(N) // L
+    mask = (blk[None, :] <= blk[:, None]).to(torch.float64)  # [i, j]
+    w_num = torch.einsum("bihd,bjhd->bhij", a, c) * mask
+    w_den = torch.einsum("bihd,bjhd->bhij", fq, fk) * mask
+    num = torch.einsum("bhij,bjhe->bihe", w_num, v) + torch.einsum("bihd,bhde->bihe", a, kv_in)
+    den = w_den.sum(-1).permute(0, 2, 1) + torch.einsum("bihd,bhd->bih", fq, ks_in)
+    out = num / (den[..., None] + eps)
+    out = out if g is None else torch.sigmoid(g) * out
+    kv_out = kv_in + torch.einsum("bnhd,bnhe->bhde", c, v)
+    ks_out = ks_in + fk.sum(dim=1)
+    return out, kv_out, ks_out
+
+
+@pytest.mark.parametrize("L,gated,roped", [(5, True, True), (4, False, True), (12, True, False), (1, True, True)])
+def test_chunked_backward_matches_autograd(L, gated, roped):
+    """Chunked gradients, including those of the carried and returned cache, against autograd
+    of the masked quadratic form; catches a prefix taken the wrong way (suffix vs prefix), a
+    chunk's own term dropped or the cache gradients left out."""
+    grid, bands = (3, 2, 2), (16, 24, 24)
+    B, N, H, D = 2, 12, 2, 64
+    q, k, v, g, do = (_randn(B, N, H, D) for _ in range(5))
+    kv_in, dkv_out = _randn(B, H, D, D), _randn(B, H, D, D)
+    ks_in, dks_out = np.abs(_randn(B, H, D)) * 4, _randn(B, H, D)
+    ts = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, g, kv_in, ks_in)]
+    out, kv_out, ks_out = _torch_chunked_forward(ts[0], ts[1], ts[2], ts[3] if gated else None, ts[4], ts[5], L,
+                                                 grid if roped else None, bands, 10000.0, 1e-6)
+    loss = (out * torch.tensor(do)).sum() + (kv_out * torch.tensor(dkv_out)).sum() + \
+        (ks_out * torch.tensor(dks_out)).sum()
+    loss.backward()
+    got = oracle.linear_attention_chunked_backward(q, k, v, do, L, g if gated else None,
+                                                   Rope3D(grid, bands) if roped else None, kv_in=kv_in,
+                                                   ksum_in=ks_in, dkv_out=dkv_out, dksum_out=dks_out)
+    for i, (x, t) in enumerate(zip(got, ts)):
+        if i == 3 and not gated:
+            assert x is None
+            continue
+        np.testing.assert_allclose(x, t.grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=str(i))
+
+
+def test_chunked_backward_matches_finite_differences():
+    """Central differences of the chunked forward oracle, cache terms included, on a tiny
+    ragged case (7 tokens in chunks of 3)."""
+    grid, bands, D = (7, 1, 1), (4, 2, 2), 8
+    B, N, H, L = 1, 7, 1, 3
+    q, k, v, g, do = (_randn(B, N, H, D) for _ in range(5))
+    kv_in, dkv_out = _randn(B, H, D, D), _randn(B, H, D, D)
+    ks_in, dks_out = np.abs(_randn(B, H, D)) * 2, _randn(B, H, D)
+    rope = Rope3D(grid, bands)
+    grads = oracle.linear_attention_chunked_backward(q, k, v, do, L, g, rope, kv_in=kv_in, ksum_in=ks_in,
+                                                     dkv_out=dkv_out, dksum_out=dks_out)
+
+    def loss(q_, k_, v_, g_, kv_, ks_):
+        o, kvo, kso = oracle.linear_attention_chunked(q_, k_, v_, L, g_, rope, kv_in=kv_, ksum_in=ks_)
+        return float(np.sum(do * o) + np.sum(dkv_out * kvo) + np.sum(dks_out * kso))
+
+    h = 1e-6
+    base = [q, k, v, g, kv_in, ks_in]
+    for which, grad in enumerate(grads):
+        for idx in np.ndindex(base[which].shape):
+            xs = [x.copy() for x in base]
+            if which < 2 and abs(xs[which][idx]) < 1e-3:
+                continue  # ReLU kink
+            xs[which][idx] += h
+            up = loss(*xs)
+            xs[which][idx] -= 2 * h
+            dn = loss(*xs)
+            assert abs((up - dn) / (2 * h) - grad[idx]) <= 1e-5 * (1.0 + abs(grad[idx])), (which, idx)
+
+
+def test_chunked_backward_one_chunk_is_bidirectional():
+    """One chunk and no cache: the chunked gradients reduce to the bidirectional ones."""
+    grid, bands = (2, 3, 2), (16, 24, 24)
+    q, k, v, g, do = (_randn(2, 12, 2, 64) for _ in range(5))
+    rope = Rope3D(grid, bands)
+    a = oracle.linear_attention_chunked_backward(q, k, v, do, 12, g, rope)
+    b = oracle.linear_attention_backward(q, k, v, do, g, rope)
+    for x, y in zip(a[:4], b):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
+
+
 def test_chunked_kv_in_is_added():
     q, k, v = (_randn(1, 6, 1, 64) for _ in range(3))
     kv_in = _randn(1, 1, 64, 64)

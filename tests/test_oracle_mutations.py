@@ -52,6 +52,14 @@ MUTATIONS = [
     ("linear_attention.py", "dden = -np.sum(dy * y, axis=-1, keepdims=True) / den",
      "dden = np.sum(dy * y, axis=-1, keepdims=True) / den"),
     ("linear_attention.py", "dphik = dc + dk_sum[:, None]", "dphik = dc"),
+    # chunked backward: prefix instead of suffix, chunk's own term dropped, returned-cache gradient dropped
+    ("linear_attention.py", "    for ci in range(len(chunks) - 1, -1, -1):", "    for ci in range(len(chunks)):"),
+    ("linear_attention.py", "        dz_key[:, sl] = gz[:, None]", "        dz_key[:, sl] = (gz - dks_chunk[ci])[:, None]"),
+    ("linear_attention.py", 'dc[:, sl] = np.einsum("bhde,bnhe->bnhd", gkv, v[:, sl])',
+     'dc[:, sl] = np.einsum("bhde,bnhe->bnhd", gkv - dkv_chunk[ci], v[:, sl])'),
+    ("linear_attention.py",
+     "gkv = np.zeros((B, H, D, D)) if dkv_out is None else np.array(dkv_out, dtype=np.float64)",
+     "gkv = np.zeros((B, H, D, D))"),
     # anchor: missing scale, softmax over the wrong axis
     ("softmax_anchor.py", "logits = scale * (q[b, rr, h, :] @ kh.T)", "logits = (q[b, rr, h, :] @ kh.T)"),
     ("softmax_anchor.py", "p = p / p.sum(axis=1, keepdims=True)", "p = p / p.sum(axis=0, keepdims=True)"),
