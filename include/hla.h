@@ -11,6 +11,9 @@
  *                            D x D state and key sum across chunks.
  *   hla_linear_attn_causal   token-causal variant: every token sees itself and
  *                            the tokens before it, plus a carried state.
+ *   hla_linear_attn_backward, hla_linear_attn_chunked_backward
+ *                            gradients of the bidirectional and block-causal
+ *                            variants (inputs, gate and carried state).
  *   hla_softmax_anchor       gated non-causal softmax attention (the periodic
  *                            full-rank anchor layer).
  *   hla_attnres_route        block attention-residual (AttnRes) depth router.
@@ -31,7 +34,9 @@
  *   exception crosses this interface. The library holds no mutable global
  *   state, so calls from several host threads are safe.
  * - Aliasing: outputs must not overlap inputs, except kv_out == kv_in and
- *   ksum_out == ksum_in in hla_linear_attn_chunked and hla_linear_attn_causal.
+ *   ksum_out == ksum_in in hla_linear_attn_chunked and hla_linear_attn_causal,
+ *   and dkv_in == dkv_out, dksum_in == dksum_out in
+ *   hla_linear_attn_chunked_backward.
  * - Numbers: HLA_BF16 tensors hold bfloat16 values, HLA_F32 tensors float.
  *   States, key sums, router queries and RoPE tables are always float.
  *   Arithmetic is float32 throughout; bf16 outputs are rounded to nearest
@@ -156,6 +161,61 @@ hla_status hla_linear_attn_causal(hla_dtype dt, int B, int N, int H, int D,
                                   const float *kv_in, const float *ksum_in,
                                   float *kv_out, float *ksum_out,
                                   void *o, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gradients of hla_linear_attn (bf16). Given the forward's inputs and dO, the
+ * gradient of a scalar loss with respect to o, it writes dq, dk, dv and dg (the
+ * latter when g is given). With s = sigmoid(g) (1 without a gate),
+ * y_i = num_i / den_i, den_i = relu(q_i) . z + eps:
+ *   dg_i = dO_i y_i s_i (1 - s_i),  dY_i = dO_i s_i
+ *   dnum_i = dY_i / den_i,  dden_i = -(dY_i . y_i) / den_i
+ *   dq_i = (R_i^T (KV dnum_i) + dden_i z) [q_i > 0]
+ *   G = sum_i a_i^T dnum_i,  Gz = sum_i dden_i relu(q_i)
+ *   dk_j = (R_j^T (G v_j) + Gz) [k_j > 0],  dv_j = G^T c_j
+ * (R_i the rotation of token i, a_i and c_i as in hla_linear_attn; the ReLU's
+ * derivative is taken as 0 at 0). The forward is recomputed, nothing of it is
+ * kept. q, k, v, g, dO, dq, dk, dv, dg: [B][N][H][D] bf16 (dt must be HLA_BF16);
+ * dg must be given exactly when g is. Products run on bf16 matrix cores with
+ * float accumulation, the D x D matrices split into bf16 high and low parts;
+ * dnum is rounded to bf16 for the sums over queries.
+ * ws: at least hla_linear_attn_backward_workspace(B, N, H, D) bytes.
+ * Errors: as hla_linear_attn, plus INVALID_ARG for null dO/dq/dk/dv or a gate
+ * given without dg (or dg without g), UNSUPPORTED for dt != HLA_BF16.
+ */
+size_t hla_linear_attn_backward_workspace(int B, int N, int H, int D);
+hla_status hla_linear_attn_backward(hla_dtype dt, int B, int N, int H, int D,
+                                    const void *q, const void *k, const void *v, const void *g,
+                                    const hla_rope3d *rope, float eps, const void *dO,
+                                    void *dq, void *dk, void *dv, void *dg,
+                                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gradients of hla_linear_attn_chunked (bf16), including the carried and the
+ * returned cache. The loss is taken as L(o) + sum(dkv_out * kv_out) +
+ * sum(dksum_out * ksum_out): dO is dL/do and dkv_out [B][H][D][D], dksum_out
+ * [B][H][D] (float; may both be NULL for zero) are the gradients reaching the
+ * returned cache. Chunk c's queries use the cache P_c, Z_c of the forward and
+ * give dq as in hla_linear_attn_backward; a key of chunk c sees the suffix sums
+ *   G_c = dkv_out + sum over chunks c' >= c of sum_{i in c'} a_i^T dnum_i
+ *   Gz_c = dksum_out + sum over chunks c' >= c of sum_{i in c'} dden_i relu(q_i)
+ * and dkv_in, dksum_in (may both be NULL) receive G_0 and Gz_0, the gradient of
+ * the carried state. kv_in, ksum_in are the forward's carried state (may both
+ * be NULL for zero). dkv_in may equal dkv_out and dksum_in may equal dksum_out.
+ * Other arguments as hla_linear_attn_backward and hla_linear_attn_chunked.
+ * ws: at least hla_linear_attn_chunked_backward_workspace(B, N, H, D,
+ * chunk_tokens) bytes.
+ * Errors: as hla_linear_attn_backward, plus INVALID_ARG for chunk_tokens <= 0
+ * or only one of each state pair given.
+ */
+size_t hla_linear_attn_chunked_backward_workspace(int B, int N, int H, int D, int chunk_tokens);
+hla_status hla_linear_attn_chunked_backward(hla_dtype dt, int B, int N, int H, int D, int chunk_tokens,
+                                            const void *q, const void *k, const void *v, const void *g,
+                                            const hla_rope3d *rope, float eps,
+                                            const float *kv_in, const float *ksum_in, const void *dO,
+                                            const float *dkv_out, const float *dksum_out,
+                                            void *dq, void *dk, void *dv, void *dg,
+                                            float *dkv_in, float *dksum_in,
+                                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Gated non-causal softmax attention, the anchor layer of the 3:1 hybrid

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhla.so")
-SOURCES = ["hla_api.cpp", "linear_attn.hip", "anchor.hip", "route.hip"]
+SOURCES = ["hla_api.cpp", "linear_attn.hip", "linear_attn_bwd.hip", "anchor.hip", "route.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

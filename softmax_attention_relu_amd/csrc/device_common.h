@@ -87,4 +87,51 @@ __device__ __forceinline__ void rotate(float &x0, float &x1, f32x2_t cs) {
   x1 = b;
 }
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Non-temporal 16-byte store of eight bf16.
+__device__ __forceinline__ void store_nt(uint16_t *p, u32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
+}
+
+// Orders this wave's LDS stores before its later LDS loads (and the reverse)
+// without a work-group barrier: LDS requests of one wave are served in order,
+// the fence keeps the compiler from moving them across.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// cos/sin of the four pairs of one 8-dim chunk. When every band width is a
+// multiple of 8 the chunk lies in one band and the four pairs are contiguous in
+// its table: two aligned 16-byte loads. Otherwise each pair is looked up alone.
+template <bool kAligned>
+struct ChunkRope {
+  RopePair p[kAligned ? 1 : 4];
+  __device__ __forceinline__ void init(const RopeArgs &r, int chunk) {
+#pragma unroll
+    for (int j = 0; j < (kAligned ? 1 : 4); ++j) p[j] = rope_pair(r, 4 * chunk + j);
+  }
+  __device__ __forceinline__ void get(const TokenPos &tp, f32x2_t cs[4]) const {
+    if constexpr (kAligned) {
+      const uint32_t pos = p[0].band == 0 ? tp.t : (p[0].band == 1 ? tp.y : tp.x);
+      const float *q = p[0].col + (size_t)pos * p[0].stride;
+      const f32x4_t a = *reinterpret_cast<const f32x4_t *>(q);
+      const f32x4_t b = *reinterpret_cast<const f32x4_t *>(q + 4);
+      cs[0] = f32x2_t{a.x, a.y};
+      cs[1] = f32x2_t{a.z, a.w};
+      cs[2] = f32x2_t{b.x, b.y};
+      cs[3] = f32x2_t{b.z, b.w};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cs[j] = rope_cs(p[j], tp);
+    }
+  }
+};
+
+// bf16 outputs: hardware exp and reciprocal (about 1 ulp); exactly 1/2 at 0.
+__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float sigmoid_exact(float x) { return 1.f / (1.f + expf(-x)); }
+
 }  // namespace hla

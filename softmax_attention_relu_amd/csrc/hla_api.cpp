@@ -82,6 +82,49 @@ hla_status linear_common(hla_dtype dt, int B, int N, int H, int D, int chunk_tok
   return launch_linear(dt, a, plan, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
 }
 
+hla_status linear_bwd_common(hla_dtype dt, int B, int N, int H, int D, int chunk_tokens, const void *q,
+                             const void *k, const void *v, const void *g, const hla_rope3d *rope, float eps,
+                             const float *kv_in, const float *ksum_in, const void *dO, const float *dkv_out,
+                             const float *dksum_out, void *dq, void *dk, void *dv, void *dg, float *dkv_in,
+                             float *dksum_in, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !dO || !dq || !dk || !dv) return HLA_ERR_INVALID_ARG;
+  if ((g == nullptr) != (dg == nullptr)) return HLA_ERR_INVALID_ARG;
+  if (!shape_ok(B, N, H) || chunk_tokens <= 0) return HLA_ERR_INVALID_ARG;
+  if ((kv_in == nullptr) != (ksum_in == nullptr)) return HLA_ERR_INVALID_ARG;
+  if ((dkv_out == nullptr) != (dksum_out == nullptr)) return HLA_ERR_INVALID_ARG;
+  if ((dkv_in == nullptr) != (dksum_in == nullptr)) return HLA_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || isinf(eps)) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16 && dt != HLA_F32) return HLA_ERR_UNSUPPORTED;
+  if (D != kD) return HLA_ERR_UNSUPPORTED;
+  if (!rope_valid(rope, N, D)) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16) return HLA_ERR_UNSUPPORTED;
+  const LinearPlan plan = plan_linear_backward(B, N, H, chunk_tokens);
+  if (!ws || ws_bytes < plan.total_bytes) return HLA_ERR_WORKSPACE;
+  LinearBwdArgs a;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.dO = dO;
+  a.rope = make_rope(rope);
+  a.eps = eps;
+  a.kv_in = kv_in;
+  a.ksum_in = ksum_in;
+  a.dkv_out = dkv_out;
+  a.dksum_out = dksum_out;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = dg;
+  a.dkv_in = dkv_in;
+  a.dksum_in = dksum_in;
+  a.ws = ws;
+  return launch_linear_backward(a, plan, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -163,6 +206,35 @@ hla_status hla_linear_attn_causal(hla_dtype dt, int B, int N, int H, int D, cons
   a.ksum_out = ksum_out;
   a.ws = ws;
   return launch_linear_causal(a, plan, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
+}
+
+size_t hla_linear_attn_backward_workspace(int B, int N, int H, int D) {
+  if (!shape_ok(B, N, H) || D != kD) return 0;
+  return plan_linear_backward(B, N, H, N).total_bytes;
+}
+
+hla_status hla_linear_attn_backward(hla_dtype dt, int B, int N, int H, int D, const void *q, const void *k,
+                                    const void *v, const void *g, const hla_rope3d *rope, float eps, const void *dO,
+                                    void *dq, void *dk, void *dv, void *dg, void *ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  return linear_bwd_common(dt, B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, dO, nullptr,
+                           nullptr, dq, dk, dv, dg, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+size_t hla_linear_attn_chunked_backward_workspace(int B, int N, int H, int D, int chunk_tokens) {
+  if (!shape_ok(B, N, H) || D != kD || chunk_tokens <= 0) return 0;
+  return plan_linear_backward(B, N, H, chunk_tokens).total_bytes;
+}
+
+hla_status hla_linear_attn_chunked_backward(hla_dtype dt, int B, int N, int H, int D, int chunk_tokens,
+                                            const void *q, const void *k, const void *v, const void *g,
+                                            const hla_rope3d *rope, float eps, const float *kv_in,
+                                            const float *ksum_in, const void *dO, const float *dkv_out,
+                                            const float *dksum_out, void *dq, void *dk, void *dv, void *dg,
+                                            float *dkv_in, float *dksum_in, void *ws, size_t ws_bytes,
+                                            hipStream_t stream) {
+  return linear_bwd_common(dt, B, N, H, D, chunk_tokens, q, k, v, g, rope, eps, kv_in, ksum_in, dO, dkv_out,
+                           dksum_out, dq, dk, dv, dg, dkv_in, dksum_in, ws, ws_bytes, stream);
 }
 
 size_t hla_softmax_anchor_workspace(int B, int N, int H, int D) {

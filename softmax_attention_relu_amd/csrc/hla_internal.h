@@ -49,7 +49,10 @@ struct LinearPlan {
   int ngroups;          // head groups of 4 (one head per wave)
   size_t part_offset, prefix_offset, total_bytes;  // workspace layout (bytes)
   size_t init_offset = 0;  // causal path: copy of the incoming state
+  size_t dnum_offset = 0, dden_offset = 0;  // gradient path: query-side intermediates
 };
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 LinearPlan plan_linear(int B, int N, int H, int chunk_tokens);
 
@@ -65,6 +68,42 @@ struct LinearArgs {
 };
 
 hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p, hipStream_t stream);
+
+// Chunked state sums: per chunk sum_j RoPE(relu(k_j))^T v_j and the key sum
+// sum_j w_j relu(k_j) (w_j = 1 without zw), then an inclusive scan over the
+// chunks (a prefix, or a suffix when reverse) starting from start_kv/start_ksum
+// (zero when null). *prefix_out (in the workspace, [B*H][n_chunks][kStateFloats])
+// receives the scan; final_kv/final_ksum its last value; init_copy the start.
+struct StateSumArgs {
+  int B, N, H;
+  const void *k, *v;
+  const float *zw;  // nullable, [B*H][N] fp32 (bf16 rows only)
+  RopeArgs rope;
+  const float *start_kv, *start_ksum;
+  float *final_kv, *final_ksum;
+  bool reverse;
+  float *init_copy;
+};
+
+hipError_t launch_state_sums(hla_dtype dt, const StateSumArgs &s, const LinearPlan &p, void *ws, hipStream_t stream,
+                             float **prefix_out);
+
+// Gradients of the bidirectional / block-causal path (bf16). dO, dq, dk, dv,
+// dg share the (B, N, H, 64) layout of q; the cache gradients are fp32.
+struct LinearBwdArgs {
+  int B, N, H;
+  const void *q, *k, *v, *g, *dO;
+  RopeArgs rope;
+  float eps;
+  const float *kv_in, *ksum_in;    // nullable carried state of the forward
+  const float *dkv_out, *dksum_out;  // nullable gradient of the returned cache
+  void *dq, *dk, *dv, *dg;
+  float *dkv_in, *dksum_in;        // nullable gradient of the carried state
+  void *ws;
+};
+
+LinearPlan plan_linear_backward(int B, int N, int H, int chunk_tokens);
+hipError_t launch_linear_backward(const LinearBwdArgs &a, const LinearPlan &p, hipStream_t stream);
 
 // Token-causal path (bf16, band widths multiples of 8): ranges of whole
 // 32-token steps as the chunks of the state build and scan.

@@ -83,6 +83,7 @@ struct Elem<false> {
 
 struct BuildArgs {
   const void *k, *v;
+  const float *zw;  // kZW: per-token weight of the key sum, [B*H][N]
   int N, H, L, n_chunks, slabs_per_chunk, ngroups;
   RopeArgs rope;
   float *part;  // [B*H][n_chunks*slabs_per_chunk][kStateFloats]
@@ -99,33 +100,6 @@ constexpr int kWaveLds32 = 2 * kD * kWRow32 * 4;
 // patterns hit 16 distinct bank groups per 16 lanes: the transposed stores
 // (rows 8 apart) and the matrix-core operand loads (16 consecutive rows).
 __device__ __forceinline__ int gran_swz(int row) { return (((row >> 5) & 1) << 1) | (((row >> 4) & 1) << 2); }
-
-// cos/sin of the four pairs of one 8-dim chunk. When every band width is a
-// multiple of 8 the chunk lies in one band and the four pairs are contiguous in
-// its table: two aligned 16-byte loads. Otherwise each pair is looked up alone.
-template <bool kAligned>
-struct ChunkRope {
-  RopePair p[kAligned ? 1 : 4];
-  __device__ __forceinline__ void init(const RopeArgs &r, int chunk) {
-#pragma unroll
-    for (int j = 0; j < (kAligned ? 1 : 4); ++j) p[j] = rope_pair(r, 4 * chunk + j);
-  }
-  __device__ __forceinline__ void get(const TokenPos &tp, f32x2_t cs[4]) const {
-    if constexpr (kAligned) {
-      const uint32_t pos = p[0].band == 0 ? tp.t : (p[0].band == 1 ? tp.y : tp.x);
-      const float *q = p[0].col + (size_t)pos * p[0].stride;
-      const f32x4_t a = *reinterpret_cast<const f32x4_t *>(q);
-      const f32x4_t b = *reinterpret_cast<const f32x4_t *>(q + 4);
-      cs[0] = f32x2_t{a.x, a.y};
-      cs[1] = f32x2_t{a.z, a.w};
-      cs[2] = f32x2_t{b.x, b.y};
-      cs[3] = f32x2_t{b.z, b.w};
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cs[j] = rope_cs(p[j], tp);
-    }
-  }
-};
 
 // RoPE of the state build for an aligned 8-dim chunk. A build lane rotates 8
 // consecutive tokens, so it reads (cos, sin) from its band's table for the
@@ -182,15 +156,6 @@ struct RopeWalk {
   }
 };
 
-// Orders this wave's LDS stores before its later LDS loads (and the reverse)
-// without a work-group barrier: LDS requests of one wave are served in order,
-// the fence keeps the compiler from moving them across.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // ---------------------------------------------------------------------------
 // State build. Wave w of a work-group owns head 4*g + w of one slab and streams
 // its 64-token tiles with no work-group barrier. The tiles of a chunk are dealt
@@ -204,8 +169,9 @@ __device__ __forceinline__ void wave_lds_fence() {
 // stores its 8x8 block transposed into the wave's LDS tiles (dim-major,
 // token-contiguous), the layout the matrix cores need because S = C^T V
 // reduces over tokens. The wave accumulates all of S (four 32x32 blocks) and
-// writes its slab's partial (S, z) record at the end.
-template <bool kBF16, bool kRope, bool kAligned>
+// writes its slab's partial (S, z) record at the end. With kZW the key sum
+// weights token j by zw_j (the gradient pass sums dden_i relu(q_i) this way).
+template <bool kBF16, bool kRope, bool kAligned, bool kZW>
 __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs a) {
   typedef Elem<kBF16> E;
   typedef typename E::T T;
@@ -231,6 +197,7 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
   const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD + dc * 8;
   const T *kp = reinterpret_cast<const T *>(a.k) + head_base;
   const T *vp = reinterpret_cast<const T *>(a.v) + head_base;
+  const float *zwp = kZW ? a.zw + (size_t)bh * a.N : nullptr;
 
   // aligned bands: walk the positions; otherwise look every pair up
   RopeWalk walk;
@@ -265,6 +232,11 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
     for (int r = 0; r < 8; ++r) vr[r] = E::load(vp + (size_t)min(base + 8 * g + r, hi - 1) * tok_stride);
 #pragma unroll
     for (int r = 0; r < 8; ++r) kr[r] = E::load(kp + (size_t)min(base + 8 * g + r, hi - 1) * tok_stride);
+    float zw[kZW ? 8 : 1];
+    if constexpr (kZW) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) zw[r] = zwp[min(base + 8 * g + r, hi - 1)];
+    }
     if constexpr (kRope && kAligned) {
       cpos = walk.coord(token_pos(a.rope, (uint32_t)min(base + 8 * g, hi - 1)));
       walk.fetch(cpos, cur);
@@ -324,7 +296,10 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         x[i] = fmaxf(x[i], 0.f);
-        zacc[i] += x[i];
+        if constexpr (kZW)
+          zacc[i] += zw[r] * x[i];
+        else
+          zacc[i] += x[i];
       }
       if constexpr (kRope && kAligned) {
         if (r > 0) {
@@ -423,7 +398,8 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Fixed-order reduction of slab partials and inclusive prefix over chunks.
+// Fixed-order reduction of slab partials and inclusive prefix over chunks
+// (inclusive suffix, from the last chunk back, for the gradient pass).
 struct ScanArgs {
   const float *part;
   int n_chunks, slabs_per_chunk;
@@ -431,6 +407,7 @@ struct ScanArgs {
   float *kv_out, *ksum_out;
   float *prefix;  // [B*H][n_chunks][kStateFloats]
   float *init;    // nullable: receives the incoming state (kv_in or zero) [B*H][kStateFloats]
+  int reverse;    // suffix sums: chunks from the last one back
 };
 
 __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
@@ -445,7 +422,8 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
   const int nsl = a.n_chunks * a.slabs_per_chunk;
   const float *p = a.part + (size_t)bh * nsl * kStateFloats + idx;
   float *pre = a.prefix + (size_t)bh * a.n_chunks * kStateFloats + idx;
-  for (int c = 0; c < a.n_chunks; ++c) {
+  for (int ci = 0; ci < a.n_chunks; ++ci) {
+    const int c = a.reverse ? a.n_chunks - 1 - ci : ci;
     // slabs are added in index order; the loads are issued eight at a time
     const float *pc = p + (size_t)c * a.slabs_per_chunk * kStateFloats;
     float s = 0.f;
@@ -520,10 +498,6 @@ struct ChunkRopeLds {
   }
 };
 
-// bf16 outputs: hardware exp and reciprocal (about 1 ulp); exactly 1/2 at 0.
-__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
-__device__ __forceinline__ float sigmoid_exact(float x) { return 1.f / (1.f + expf(-x)); }
-
 // ---------------------------------------------------------------------------
 // Apply. Wave w of a work-group owns head 4*g + w of one part of a chunk and
 // walks it 32 tokens at a time; the 32-token steps of a chunk are dealt out to
@@ -541,12 +515,6 @@ __device__ __forceinline__ float sigmoid_exact(float x) { return 1.f / (1.f + ex
 // m = 8i + 4h + j of a 32x32 product holds dim 16h + 4i + j), so the 16
 // results of a lane are 16 consecutive dims.
 constexpr int kStageRow = kD + 8;  // bf16 per staged token row (144 bytes)
-
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void store_nt(uint16_t *p, u32x4_t v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
-}
 
 template <int kRopeMode, bool kGate>
 __global__ __launch_bounds__(256, kRopeMode == kRopePair ? 1 : 2) void la_apply_bf16_kernel(ApplyArgs a) {
@@ -828,7 +796,6 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
   }
 }
 
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------------------
 // Token-causal apply (bf16). Token i sees the state of every token j <= i:
@@ -1152,21 +1119,21 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
   }
 }
 
-template <bool kBF16, bool kRope, bool kAligned>
+template <bool kBF16, bool kRope, bool kAligned, bool kZW>
 hipError_t launch_build(dim3 grid, const BuildArgs &ba, hipStream_t stream) {
   const size_t lds = 4 * (size_t)(kBF16 ? kWaveLds16 : kWaveLds32);
-  const void *fn = reinterpret_cast<const void *>(&la_build_kernel<kBF16, kRope, kAligned>);
+  const void *fn = reinterpret_cast<const void *>(&la_build_kernel<kBF16, kRope, kAligned, kZW>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((la_build_kernel<kBF16, kRope, kAligned>), grid, dim3(256), lds, stream, ba);
+  hipLaunchKernelGGL((la_build_kernel<kBF16, kRope, kAligned, kZW>), grid, dim3(256), lds, stream, ba);
   return hipSuccess;
 }
 
-template <bool kBF16>
+template <bool kBF16, bool kZW>
 hipError_t launch_build_any(const RopeArgs &r, dim3 grid, const BuildArgs &ba, hipStream_t stream) {
-  if (!r.enabled) return launch_build<kBF16, false, false>(grid, ba, stream);
-  if (r.aligned) return launch_build<kBF16, true, true>(grid, ba, stream);
-  return launch_build<kBF16, true, false>(grid, ba, stream);
+  if (!r.enabled) return launch_build<kBF16, false, false, kZW>(grid, ba, stream);
+  if (r.aligned) return launch_build<kBF16, true, true, kZW>(grid, ba, stream);
+  return launch_build<kBF16, true, false, kZW>(grid, ba, stream);
 }
 
 template <int kRopeMode>
@@ -1216,29 +1183,34 @@ LinearPlan plan_linear(int B, int N, int H, int chunk_tokens) {
   return p;
 }
 
-// State build and scan shared by the bidirectional, chunked and causal paths;
-// *prefix_out receives the inclusive prefix per chunk.
-static hipError_t build_and_scan(hla_dtype dt, const LinearArgs &a, const LinearPlan &p, hipStream_t stream,
-                                 float **prefix_out, float *init = nullptr) {
-  const int heads = a.B * a.H;
-  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(a.ws) + p.part_offset);
-  float *prefix = reinterpret_cast<float *>(reinterpret_cast<char *>(a.ws) + p.prefix_offset);
+hipError_t launch_state_sums(hla_dtype dt, const StateSumArgs &sa_in, const LinearPlan &p, void *ws,
+                             hipStream_t stream, float **prefix_out) {
+  const int heads = sa_in.B * sa_in.H;
+  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + p.part_offset);
+  float *prefix = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + p.prefix_offset);
+  if (sa_in.zw && dt != HLA_BF16) return hipErrorInvalidValue;
 
   BuildArgs ba;
-  ba.k = a.k;
-  ba.v = a.v;
-  ba.N = a.N;
-  ba.H = a.H;
+  ba.k = sa_in.k;
+  ba.v = sa_in.v;
+  ba.zw = sa_in.zw;
+  ba.N = sa_in.N;
+  ba.H = sa_in.H;
   ba.L = p.chunk_len;
   ba.n_chunks = p.n_chunks;
   ba.slabs_per_chunk = p.slabs_per_chunk;
   ba.ngroups = p.ngroups;
-  ba.rope = a.rope;
+  ba.rope = sa_in.rope;
   ba.part = part;
-  const dim3 bgrid(p.n_chunks * p.slabs_per_chunk * p.ngroups, a.B);
+  const dim3 bgrid(p.n_chunks * p.slabs_per_chunk * p.ngroups, sa_in.B);
   {
-    const hipError_t e = dt == HLA_BF16 ? launch_build_any<true>(a.rope, bgrid, ba, stream)
-                                        : launch_build_any<false>(a.rope, bgrid, ba, stream);
+    hipError_t e;
+    if (dt != HLA_BF16)
+      e = launch_build_any<false, false>(sa_in.rope, bgrid, ba, stream);
+    else if (sa_in.zw)
+      e = launch_build_any<true, true>(sa_in.rope, bgrid, ba, stream);
+    else
+      e = launch_build_any<true, false>(sa_in.rope, bgrid, ba, stream);
     if (e != hipSuccess) return e;
   }
   hipError_t e = hipGetLastError();
@@ -1248,17 +1220,39 @@ static hipError_t build_and_scan(hla_dtype dt, const LinearArgs &a, const Linear
   sa.part = part;
   sa.n_chunks = p.n_chunks;
   sa.slabs_per_chunk = p.slabs_per_chunk;
-  sa.kv_in = a.kv_in;
-  sa.ksum_in = a.ksum_in;
-  sa.kv_out = a.kv_out;
-  sa.ksum_out = a.ksum_out;
+  sa.kv_in = sa_in.start_kv;
+  sa.ksum_in = sa_in.start_ksum;
+  sa.kv_out = sa_in.final_kv;
+  sa.ksum_out = sa_in.final_ksum;
   sa.prefix = prefix;
-  sa.init = init;
+  sa.init = sa_in.init_copy;
+  sa.reverse = sa_in.reverse ? 1 : 0;
   hipLaunchKernelGGL(la_scan_kernel, dim3((kStateFloats + 255) / 256, heads), dim3(256), 0, stream, sa);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   *prefix_out = prefix;
   return hipSuccess;
+}
+
+// State build and scan of the forward paths; *prefix_out receives the
+// inclusive prefix per chunk.
+static hipError_t build_and_scan(hla_dtype dt, const LinearArgs &a, const LinearPlan &p, hipStream_t stream,
+                                 float **prefix_out, float *init = nullptr) {
+  StateSumArgs s;
+  s.B = a.B;
+  s.N = a.N;
+  s.H = a.H;
+  s.k = a.k;
+  s.v = a.v;
+  s.zw = nullptr;
+  s.rope = a.rope;
+  s.start_kv = a.kv_in;
+  s.start_ksum = a.ksum_in;
+  s.final_kv = a.kv_out;
+  s.final_ksum = a.ksum_out;
+  s.reverse = false;
+  s.init_copy = init;
+  return launch_state_sums(dt, s, p, a.ws, stream, prefix_out);
 }
 
 hipError_t launch_linear(hla_dtype dt, const LinearArgs &a, const LinearPlan &p, hipStream_t stream) {

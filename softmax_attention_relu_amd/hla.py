@@ -31,6 +31,10 @@ EXPORTS = (
     "hla_linear_attn_chunked",
     "hla_linear_attn_causal_workspace",
     "hla_linear_attn_causal",
+    "hla_linear_attn_backward_workspace",
+    "hla_linear_attn_backward",
+    "hla_linear_attn_chunked_backward_workspace",
+    "hla_linear_attn_chunked_backward",
     "hla_softmax_anchor_workspace",
     "hla_softmax_anchor",
     "hla_attnres_route",
@@ -81,6 +85,20 @@ def lib() -> ctypes.CDLL:
                                              c_void_p, POINTER(hla_rope3d), c_float, c_void_p, c_void_p, c_void_p,
                                              c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.hla_linear_attn_causal.restype = c_int
+        L.hla_linear_attn_backward_workspace.argtypes = [c_int, c_int, c_int, c_int]
+        L.hla_linear_attn_backward_workspace.restype = c_size_t
+        L.hla_linear_attn_backward.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                               c_void_p, POINTER(hla_rope3d), c_float, c_void_p, c_void_p, c_void_p,
+                                               c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.hla_linear_attn_backward.restype = c_int
+        L.hla_linear_attn_chunked_backward_workspace.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        L.hla_linear_attn_chunked_backward_workspace.restype = c_size_t
+        L.hla_linear_attn_chunked_backward.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                                                       c_void_p, c_void_p, POINTER(hla_rope3d), c_float, c_void_p,
+                                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                                       c_void_p]
+        L.hla_linear_attn_chunked_backward.restype = c_int
         L.hla_softmax_anchor_workspace.argtypes = [c_int, c_int, c_int, c_int]
         L.hla_softmax_anchor_workspace.restype = c_size_t
         L.hla_softmax_anchor.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -249,6 +267,56 @@ def hla_linear_attn_causal(q, k, v, g=None, rope: Rope3D | None = None, eps: flo
                                       _ptr(ksum_out), _ptr(o), _ptr(ws), nbytes, _stream(stream))
     _check(st, "hla_linear_attn_causal")
     return o
+
+
+def hla_linear_attn_backward_workspace(B: int, N: int, H: int, D: int = 64) -> int:
+    return int(lib().hla_linear_attn_backward_workspace(B, N, H, D))
+
+
+def hla_linear_attn_backward(q, k, v, do, g=None, rope: Rope3D | None = None, eps: float = 1e-6, dq=None, dk=None,
+                             dv=None, dg=None, ws=None, stream=None):
+    """Gradients of the bidirectional linear attention (bf16); returns (dq, dk, dv, dg), dg None without g."""
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if g is not None and dg is None:
+        dg = torch.empty_like(g)
+    ws, nbytes = _workspace(hla_linear_attn_backward_workspace(B, N, H, D), q.device, ws)
+    st = lib().hla_linear_attn_backward(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                        _rope_ptr(rope), float(eps), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                        _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_linear_attn_backward")
+    return dq, dk, dv, dg
+
+
+def hla_linear_attn_chunked_backward_workspace(B: int, N: int, H: int, D: int, chunk_tokens: int) -> int:
+    return int(lib().hla_linear_attn_chunked_backward_workspace(B, N, H, D, chunk_tokens))
+
+
+def hla_linear_attn_chunked_backward(q, k, v, do, chunk_tokens: int, g=None, rope: Rope3D | None = None,
+                                     eps: float = 1e-6, kv_in=None, ksum_in=None, dkv_out=None, dksum_out=None,
+                                     dq=None, dk=None, dv=None, dg=None, dkv_in=None, dksum_in=None, ws=None,
+                                     stream=None):
+    """Gradients of the block-causal linear attention (bf16), cache terms included.
+
+    Returns (dq, dk, dv, dg); the carried state's gradient goes to dkv_in/dksum_in when given.
+    """
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if g is not None and dg is None:
+        dg = torch.empty_like(g)
+    ws, nbytes = _workspace(hla_linear_attn_chunked_backward_workspace(B, N, H, D, chunk_tokens), q.device, ws)
+    st = lib().hla_linear_attn_chunked_backward(
+        _dtype_code(q), B, N, H, D, int(chunk_tokens), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _rope_ptr(rope),
+        float(eps), _ptr(kv_in), _ptr(ksum_in), _ptr(do), _ptr(dkv_out), _ptr(dksum_out), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dg), _ptr(dkv_in), _ptr(dksum_in), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_linear_attn_chunked_backward")
+    return dq, dk, dv, dg
 
 
 def hla_softmax_anchor_workspace(B: int, N: int, H: int, D: int = 64) -> int:

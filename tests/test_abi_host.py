@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 15
     assert sorted(hla.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -146,6 +146,40 @@ def test_causal_validation(L):
     assert call(ws_bytes=16) == E.HLA_ERR_WORKSPACE
     assert hla.hla_linear_attn_causal_workspace(1, 75600, 32, 64) > 0
     assert hla.hla_linear_attn_causal_workspace(1, 75600, 32, 48) == 0
+
+
+def test_backward_validation(L):
+    E = hla
+
+    def call(dt=0, rope=None, g=None, dg=None, dO=FAKE, dk=FAKE, ws_bytes=1 << 40, L_=8, kv_in=None, ks_in=None,
+             dkv_out=None, dks_out=None, dkv_in=None, dks_in=None, chunked=True):
+        if not chunked:
+            return L.hla_linear_attn_backward(dt, 1, 8, 1, 64, FAKE, FAKE, FAKE, g,
+                                              ctypes.byref(rope) if rope else None, 1e-6, dO, FAKE, dk, FAKE, dg,
+                                              FAKE, ws_bytes, None)
+        return L.hla_linear_attn_chunked_backward(dt, 1, 8, 1, 64, L_, FAKE, FAKE, FAKE, g,
+                                                  ctypes.byref(rope) if rope else None, 1e-6, kv_in, ks_in, dO,
+                                                  dkv_out, dks_out, FAKE, dk, FAKE, dg, dkv_in, dks_in, FAKE,
+                                                  ws_bytes, None)
+
+    for chunked in (False, True):
+        assert call(dO=None, chunked=chunked) == E.HLA_ERR_INVALID_ARG
+        assert call(dk=None, chunked=chunked) == E.HLA_ERR_INVALID_ARG
+        assert call(g=FAKE, chunked=chunked) == E.HLA_ERR_INVALID_ARG  # gate without dg
+        assert call(dg=FAKE, chunked=chunked) == E.HLA_ERR_INVALID_ARG  # dg without gate
+        assert call(dt=1, chunked=chunked) == E.HLA_ERR_UNSUPPORTED  # bf16 only
+        assert call(rope=_rope((2, 2, 3), (16, 24, 24)), chunked=chunked) == E.HLA_ERR_INVALID_ARG  # grid != N
+        assert call(ws_bytes=16, chunked=chunked) == E.HLA_ERR_WORKSPACE
+    assert call(L_=0) == E.HLA_ERR_INVALID_ARG
+    assert call(kv_in=FAKE) == E.HLA_ERR_INVALID_ARG
+    assert call(dks_out=FAKE) == E.HLA_ERR_INVALID_ARG
+    assert call(dkv_in=FAKE) == E.HLA_ERR_INVALID_ARG
+    # workspace: forward state regions plus bf16 dnum and fp32 dden
+    n = hla.hla_linear_attn_backward_workspace(1, 75600, 32, 64)
+    assert n >= hla.hla_linear_attn_workspace(1, 75600, 32, 64) + 75600 * 32 * (64 * 2 + 4)
+    assert hla.hla_linear_attn_backward_workspace(1, 75600, 32, 48) == 0
+    assert hla.hla_linear_attn_chunked_backward_workspace(1, 100, 2, 64, 0) == 0
+    assert hla.hla_linear_attn_chunked_backward_workspace(1, 100, 2, 64, 30) > 0
 
 
 def test_anchor_validation(L):
