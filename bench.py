@@ -10,8 +10,10 @@ seeded synthetic tensors already resident in HBM.
 Printed: one JSON line. ``value`` is the linear-attention token throughput at
 the 720p/5s shape (tokens per second of one layer, B*N / mean layer time);
 ``ms_per_step`` is the wall time of a whole group. Per-call times come from
-HIP events recorded on the stream the library launches on. ``legs`` adds the
-block-causal 720p/60s case (N=867600, chunks of 36000) timed the same way.
+HIP events recorded on the stream the library launches on. ``legs`` adds, timed
+the same way: the token-causal and the backward (gradient) pass of the first
+720p/5s linear layer, the block-causal 720p/60s case (N=867600, chunks of
+36000) and the same sequence streamed block by block for a cond/uncond pair.
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the linear
 layer (a few heads) on the host cores.
 
@@ -192,7 +194,7 @@ def main() -> int:
                     ev["anchor"][1].record()
 
     if args.profile_pass:
-        log("[bench] profile pass: one step, one token-causal call, one 720p/60s chunked call, "
+        log("[bench] profile pass: one step, one token-causal call, one backward call, one 720p/60s chunked call, "
             "then a 1 GiB copy (calibration)")
         step()
         torch.cuda.synchronize()
@@ -200,6 +202,10 @@ def main() -> int:
             cw0, cx0 = lin[0]
             hla.hla_linear_attn_causal(cx0["q"], cx0["k"], cx0["v"], cx0["g"], cx0["rope"], cw0.eps)
             torch.cuda.synchronize()
+            bdo = dev(synth.randn(cw0.seed, (cw0.B, cw0.N, cw0.H, cw0.D), stream=4))
+            hla.hla_linear_attn_backward(cx0["q"], cx0["k"], cx0["v"], bdo, cx0["g"], cx0["rope"], cw0.eps)
+            torch.cuda.synchronize()
+            del bdo
         if not args.no_legs:
             del lin, routes
             torch.cuda.empty_cache()
@@ -317,6 +323,42 @@ def main() -> int:
             "algorithmic_bytes": lin_bytes}
         log(f"[bench] token-causal 720p/5s: {ca_ms:.3f} ms")
         del cws, co
+
+    # ---------------- backward leg: gradients of the first 720p/5s linear layer (gated, RoPE)
+    if not args.no_legs:
+        bx = lin[0][1]
+        bdo = dev(synth.randn(w0.seed, (w0.B, w0.N, w0.H, w0.D), stream=4))
+        bws = torch.empty(hla.hla_linear_attn_backward_workspace(w0.B, w0.N, w0.H, w0.D), dtype=torch.uint8,
+                          device="cuda")
+        bouts = [torch.empty_like(bx["q"]) for _ in range(4)]
+
+        def bwd_call():
+            hla.hla_linear_attn_backward(bx["q"], bx["k"], bx["v"], bdo, bx["g"], bx["rope"], w0.eps, dq=bouts[0],
+                                         dk=bouts[1], dv=bouts[2], dg=bouts[3], ws=bws)
+
+        bwd_call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            bwd_call()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        bw_ms = float(np.mean(times))
+        # algorithmic: Q, K, V, G, dO read once and dQ, dK, dV, dG written once
+        bw_bytes = tokh * 64 * 2 * 9
+        # what the four-kernel schedule moves: K, V (state) + Q, G, dO in, dQ, dG, dnum out + Q, dnum (gradient
+        # state) + K, V in, dK, dV out, bf16; plus dden fp32 written and read
+        bw_sched = tokh * 64 * 2 * 16 + tokh * 4 * 2
+        out.setdefault("legs", {})["backward_720p5s"] = {
+            "N": w0.N, "ms": bw_ms, "tokens_per_s": w0.B * w0.N / (bw_ms * 1e-3),
+            "hbm_gbs": bw_bytes / (bw_ms * 1e-3) / 1e9, "hbm_frac": bw_bytes / (bw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": bw_bytes, "schedule_bytes": bw_sched,
+            "schedule_gbs": bw_sched / (bw_ms * 1e-3) / 1e9}
+        log(f"[bench] backward 720p/5s: {bw_ms:.3f} ms")
+        del bws, bouts, bdo
 
     # ---------------- block-causal 720p/60s leg
     if not args.no_legs:
