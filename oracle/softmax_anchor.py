@@ -54,3 +54,49 @@ def softmax_anchor(q, k, v, g=None, scale: float | None = None, rows=None, row_b
     if g is not None:
         out = _sigmoid(np.asarray(g, dtype=np.float64)[:, rows]) * out
     return out
+
+
+def softmax_anchor_block_sparse(q, k, v, blocks, counts, g=None, scale: float | None = None, q_block: int = 128,
+                                k_block: int = 64, rows=None):
+    """Block-sparse gated softmax anchor, fp64 (parity unpinned against the pages).
+
+    The pages name a sparse anchor (SANA-Video 2.0 summary, efficiency
+    paragraph: the last stage of its engine) without its pattern; the reading
+    is a caller-given block pattern. Query row i lies in query block
+    r = i // q_block; for each (b, h, r) the first counts[b, h, r] entries of
+    blocks[b, h, r, :] name key blocks m, and the row attends to the keys
+    m * k_block <= j < min(N, (m + 1) * k_block) of every named block (entries
+    outside [0, ceil(N / k_block)) name nothing). With K_r that key set:
+
+        o_i = sigmoid(g_i) * sum_{j in K_r} softmax_{j in K_r}(scale * q_i . k_j) v_j
+
+    and o_i = 0 when K_r is empty. Named blocks are taken as a set; the GPU
+    kernel expects them distinct.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    blocks = np.asarray(blocks)
+    counts = np.asarray(counts)
+    B, N, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    n_kb = -(-N // k_block)
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    out = np.zeros((B, len(rows), H, D))
+    for b in range(B):
+        for h in range(H):
+            for idx, i in enumerate(rows):
+                r = i // q_block
+                named = {int(m) for m in blocks[b, h, r, :counts[b, h, r]] if 0 <= m < n_kb}
+                keys = np.array(sorted(j for m in named for j in range(m * k_block, min(N, (m + 1) * k_block))),
+                                dtype=np.int64)
+                if keys.size == 0:
+                    continue
+                logits = scale * (k[b, keys, h, :] @ q[b, i, h, :])
+                p = np.exp(logits - logits.max())
+                p = p / p.sum()
+                out[b, idx, h, :] = p @ v[b, keys, h, :]
+    if g is not None:
+        out = _sigmoid(np.asarray(g, dtype=np.float64)[:, rows]) * out
+    return out

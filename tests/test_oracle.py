@@ -577,6 +577,58 @@ def test_anchor_matches_torch_sdpa_f64():
     np.testing.assert_allclose(got, ref.numpy().transpose(0, 2, 1, 3), rtol=1e-11, atol=1e-13)
 
 
+def test_sparse_anchor_matches_python_loops():
+    """Tiny block-sparse case against loops over the allowed keys (query blocks of 4, key blocks of 3)."""
+    B, N, H, D = 1, 10, 2, 4
+    q, k, v, g = (_randn(B, N, H, D) for _ in range(4))
+    # [b][h][query block][entry]; 9, -1 and 7 name nothing (4 key blocks)
+    blocks = np.array([[[[2, 0, 9], [1, -1, 7], [3, 0, 0]], [[0, 1, 2], [1, 0, 0], [2, 3, 1]]]])
+    counts = np.array([[[3, 3, 1], [0, 1, 3]]])
+    got = oracle.softmax_anchor_block_sparse(q, k, v, blocks, counts, g, scale=0.5, q_block=4, k_block=3)
+    for h in range(H):
+        for i in range(N):
+            r = i // 4
+            named = {m for m in blocks[0, h, r, :counts[0, h, r]] if 0 <= m < 4}
+            keys = [j for j in range(N) if j // 3 in named]
+            if not keys:
+                assert np.all(got[0, i, h] == 0)
+                continue
+            ls = [0.5 * sum(q[0, i, h, d] * k[0, j, h, d] for d in range(D)) for j in keys]
+            m = max(ls)
+            e = [math.exp(x - m) for x in ls]
+            for c in range(D):
+                o = sum(ej / sum(e) * v[0, j, h, c] for ej, j in zip(e, keys))
+                o /= 1 + math.exp(-g[0, i, h, c])
+                assert got[0, i, h, c] == pytest.approx(o, rel=1e-12, abs=1e-15)
+
+
+def test_sparse_anchor_all_blocks_is_dense():
+    """Every key block named (any order, plus entries that name nothing) gives the dense anchor."""
+    B, N, H, D = 2, 300, 2, 64
+    q, k, v, g = (_randn(B, N, H, D) for _ in range(4))
+    n_qb, n_kb = 3, 5
+    blocks = np.full((B, H, n_qb, n_kb + 2), -1, dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            for r in range(n_qb):
+                blocks[b, h, r, :n_kb + 1] = np.append(RNG.permutation(n_kb), n_kb + 3)
+    counts = np.full((B, H, n_qb), n_kb + 2)
+    got = oracle.softmax_anchor_block_sparse(q, k, v, blocks, counts, g, scale=0.125)
+    np.testing.assert_allclose(got, oracle.softmax_anchor(q, k, v, g, scale=0.125), rtol=1e-10, atol=1e-13)
+
+
+def test_sparse_anchor_one_block_and_empty():
+    """One named block equals the dense anchor over that block's keys; no named block gives zero."""
+    B, N, H, D = 1, 200, 1, 64
+    q, k, v = (_randn(B, N, H, D) for _ in range(3))
+    blocks = np.array([[[[3], [0]]]])  # query block 0 -> keys 192..199 (ragged), block 1 -> keys 0..63
+    counts = np.array([[[1, 0]]])
+    got = oracle.softmax_anchor_block_sparse(q, k, v, blocks, counts, scale=0.125)
+    ref = oracle.softmax_anchor(q, k[:, 192:], v[:, 192:], scale=0.125, rows=np.arange(128))
+    np.testing.assert_allclose(got[:, :128], ref, rtol=1e-12, atol=1e-14)
+    assert np.all(got[:, 128:] == 0)
+
+
 def test_anchor_special_cases():
     B, N, H, D = 1, 16, 1, 64
     q, v = _randn(B, N, H, D), _randn(B, N, H, D)

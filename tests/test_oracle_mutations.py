@@ -63,6 +63,9 @@ MUTATIONS = [
     # anchor: missing scale, softmax over the wrong axis
     ("softmax_anchor.py", "logits = scale * (q[b, rr, h, :] @ kh.T)", "logits = (q[b, rr, h, :] @ kh.T)"),
     ("softmax_anchor.py", "p = p / p.sum(axis=1, keepdims=True)", "p = p / p.sum(axis=0, keepdims=True)"),
+    # block-sparse anchor: last key of a block dropped, query block taken with the key block size
+    ("softmax_anchor.py", "range(m * k_block, min(N, (m + 1) * k_block))", "range(m * k_block, min(N, (m + 1) * k_block - 1))"),
+    ("softmax_anchor.py", "                r = i // q_block", "                r = i // k_block"),
     # router: RMSNorm dropped, eps dropped, sum instead of mean
     ("attnres_router.py", "normed = v / rms", "normed = v"),
     ("attnres_router.py", "np.mean(v * v, axis=-1, keepdims=True) + eps", "np.mean(v * v, axis=-1, keepdims=True)"),
