@@ -360,6 +360,43 @@ def main() -> int:
         log(f"[bench] backward 720p/5s: {bw_ms:.3f} ms")
         del bws, bouts, bdo
 
+    # ---------------- block-sparse anchor leg: 720p/5s with a local-window pattern
+    if not args.no_legs:
+        sw = synth.SPARSE_ANCHOR_720P5S
+        sx = {k: dev(v) for k, v in sw.draw().items()}
+        sb, sc = synth.block_window_pattern(sw.B, sw.H, sw.N, *synth.SPARSE_ANCHOR_WINDOW)
+        # query-key pairs visited: rows of each query block x keys of its named blocks
+        rows_per_qb = np.minimum(128, sw.N - 128 * np.arange(sb.shape[2]))
+        keys_per_blk = np.minimum(64, sw.N - 64 * np.arange(-(-sw.N // 64)))
+        pairs = float(sum(int(rows_per_qb[r]) * int(keys_per_blk[sb[b, h, r, :sc[b, h, r]]].sum())
+                          for b in range(sw.B) for h in range(sw.H) for r in range(sb.shape[2])))
+        sbt, sct = torch.from_numpy(sb).cuda(), torch.from_numpy(sc).cuda()
+        so = torch.empty_like(sx["q"])
+        sws = torch.empty(hla.hla_softmax_anchor_workspace(sw.B, sw.N, sw.H, sw.D), dtype=torch.uint8, device="cuda")
+
+        def sparse_call():
+            hla.hla_softmax_anchor_block_sparse(sx["q"], sx["k"], sx["v"], sbt, sct, sx["g"], sw.scale, o=so, ws=sws)
+
+        sparse_call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            sparse_call()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        sp_ms = float(np.mean(times))
+        sp_tf = 4.0 * sw.D * pairs / (sp_ms * 1e-3) / 1e12
+        out.setdefault("legs", {})["sparse_anchor_720p5s"] = {
+            "N": sw.N, "pattern": "window +-72 key blocks + 4 global (64-key blocks, 128-row query blocks)",
+            "density": pairs / (sw.B * sw.H * float(sw.N) ** 2), "ms": sp_ms, "visited_pair_tflops": sp_tf,
+            "mfma_frac": sp_tf / BF16_PEAK_TFLOPS}
+        log(f"[bench] sparse anchor 720p/5s: {sp_ms:.3f} ms, density {pairs / (sw.B * sw.H * float(sw.N) ** 2):.3f}, "
+            f"{sp_tf:.0f} TFLOP/s on visited pairs")
+        del sx, so, sws, sbt, sct
+
     # ---------------- block-causal 720p/60s leg
     if not args.no_legs:
         del lin, routes

@@ -16,6 +16,8 @@
  *                            variants (inputs, gate and carried state).
  *   hla_softmax_anchor       gated non-causal softmax attention (the periodic
  *                            full-rank anchor layer).
+ *   hla_softmax_anchor_block_sparse
+ *                            the anchor restricted to caller-given key blocks.
  *   hla_attnres_route        block attention-residual (AttnRes) depth router.
  *
  * Conventions shared by every entry point
@@ -234,6 +236,32 @@ size_t hla_softmax_anchor_workspace(int B, int N, int H, int D);
 hla_status hla_softmax_anchor(hla_dtype dt, int B, int N, int H, int D,
                               const void *q, const void *k, const void *v, const void *g,
                               float scale, void *o, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Block-sparse form of hla_softmax_anchor. The pages name a sparse anchor
+ * (SANA-Video 2.0 summary, efficiency paragraph) without its pattern, so the
+ * pattern is an input. Query rows form blocks of HLA_SPARSE_Q_BLOCK = 128
+ * (block r: rows [128 r, min(128 (r+1), N))), keys blocks of
+ * HLA_SPARSE_K_BLOCK = 64. For each (b, h, r), with nqb = ceil(N / 128):
+ *   counts[(b H + h) nqb + r]                    number of entries used
+ *   blocks[((b H + h) nqb + r) max_blocks + m]   key block named by entry m
+ * and every row of block r attends to the keys of the named blocks only:
+ *   o_i = sigmoid(g_i) * sum_{j in K_r} softmax_{j in K_r}(scale q_i . k_j) v_j,
+ * o_i = 0 when K_r is empty. blocks and counts are int32 DEVICE arrays. Counts
+ * are clamped to [0, max_blocks]; entries outside [0, ceil(N / 64)) name
+ * nothing and are skipped; named blocks must be distinct (a repeated entry is
+ * visited twice, giving an unspecified result but no fault). Tiles are visited
+ * in list order. Other arguments, workspace and numerics as hla_softmax_anchor
+ * (same workspace size).
+ * Errors: as hla_softmax_anchor, plus INVALID_ARG for null blocks/counts or
+ * max_blocks <= 0.
+ */
+#define HLA_SPARSE_Q_BLOCK 128
+#define HLA_SPARSE_K_BLOCK 64
+hla_status hla_softmax_anchor_block_sparse(hla_dtype dt, int B, int N, int H, int D,
+                                           const void *q, const void *k, const void *v, const void *g,
+                                           float scale, const int *blocks, const int *counts, int max_blocks,
+                                           void *o, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Block attention-residual router (SANA-Video 2.0 summary, method section,

@@ -39,6 +39,8 @@ constexpr int kVRow = kBK + 8;     // bf16 per LDS row of V^T (144 bytes)
 constexpr float kLazy = 8.0f;      // lazy max threshold, log2 units
 constexpr int kWaves = 16;         // waves per work-group, 32 query rows each
 constexpr int kMinWaves = 4;       // waves per SIMD the forward kernel is compiled for
+static_assert(kSparseKBlock == kBK, "a named key block is one tile");
+static_assert(kSparseQBlock % 32 == 0, "a query block is whole waves of 32 rows");
 
 // Key position inside a group of 16 with bits 2 and 3 swapped. With this
 // order, the 8 keys a lane feeds to one 32x32x16 product (keys 4h..4h+3 and
@@ -100,13 +102,19 @@ struct FwdArgs {
   uint16_t *o;
   int N, H, npad;
   float c;  // scale * log2(e)
+  // block-sparse form: key tiles named per (b*H + h, query block), [..][max_blocks]
+  const int *blocks, *counts;
+  int n_qb, max_blocks;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // The row sum adds the bf16-rounded P with v_dot2 (two terms per
 // instruction): the normaliser uses the same weights as the P.V product.
-template <int WAVES, int MINW>
+// kSparse: the work-group's query rows form one query block and visit only
+// the 64-key tiles named for it (entries outside the key range are skipped);
+// otherwise every tile in order.
+template <int WAVES, int MINW, bool kSparse>
 __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a) {
   constexpr int kThreads = 64 * WAVES;
   // 16-byte chunks of K (and of V^T) per thread per tile: 512 chunks each
@@ -173,12 +181,31 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
   float mref = -INFINITY, lsum = 0.f;
 
   const int ntiles = (a.N + kBK - 1) / kBK;
-  load_tile(0);
-  store_tile(0);
+  // position i of the visiting order -> key tile; next(i): first usable position >= i
+  const int *list = nullptr;
+  int cnt = ntiles;
+  if constexpr (kSparse) {
+    const size_t qblk = (size_t)bh * a.n_qb + blockIdx.x;
+    list = a.blocks + qblk * a.max_blocks;
+    cnt = min(max(a.counts[qblk], 0), a.max_blocks);
+  }
+  auto tile_of = [&](int i) { return kSparse ? list[i] : i; };
+  auto next = [&](int i) {
+    if constexpr (kSparse) {
+      while (i < cnt && (unsigned)list[i] >= (unsigned)ntiles) ++i;
+    }
+    return i;
+  };
+  int pos = next(0);
+  if (pos < cnt) {
+    load_tile(tile_of(pos));
+    store_tile(0);
+  }
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+  for (int buf = 0; pos < cnt; buf ^= 1) {
+    const int t = tile_of(pos);
+    const int pnext = next(pos + 1);
+    if (pnext < cnt) load_tile(tile_of(pnext));
 
     // S^T = K Q^T for the 64 keys of this tile
     f32x16_t sacc[2];
@@ -268,16 +295,17 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
           oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kb][u], oacc[mb], 0, 0, 0);
         }
 
-    if (t + 1 < ntiles) {
+    if (pnext < cnt) {
       store_tile(buf ^ 1);  // the other buffer was last read two tiles ago
       __syncthreads();
     }
+    pos = pnext;
   }
 
   // normalise, gate, store: lane holds row tl, dims 32*mb + 8*i + 4*half + j
   const int n = q0 + tl;
   const float l = lsum + __shfl_xor(lsum, 32);
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;  // no key visited: the output is 0
   if (n < a.N) {
     const size_t row = head_base + (size_t)n * tok_stride;
 #pragma unroll
@@ -330,8 +358,18 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   fa.H = a.H;
   fa.npad = npad;
   fa.c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves>), dim3((a.N + 32 * kWaves - 1) / (32 * kWaves), heads),
-                     dim3(64 * kWaves), 0, stream, fa);
+  fa.blocks = a.blocks;
+  fa.counts = a.counts;
+  fa.max_blocks = a.max_blocks;
+  if (a.blocks) {
+    fa.n_qb = (a.N + kSparseQBlock - 1) / kSparseQBlock;
+    hipLaunchKernelGGL((anchor_fwd_kernel<kSparseQBlock / 32, kMinWaves, true>), dim3(fa.n_qb, heads),
+                       dim3(2 * kSparseQBlock), 0, stream, fa);
+  } else {
+    fa.n_qb = 0;
+    hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, false>),
+                       dim3((a.N + 32 * kWaves - 1) / (32 * kWaves), heads), dim3(64 * kWaves), 0, stream, fa);
+  }
   return hipGetLastError();
 }
 

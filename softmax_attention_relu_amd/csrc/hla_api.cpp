@@ -7,6 +7,9 @@
 
 using namespace hla;
 
+static_assert(kSparseQBlock == HLA_SPARSE_Q_BLOCK && kSparseKBlock == HLA_SPARSE_K_BLOCK,
+              "block sizes of the sparse anchor as declared in hla.h");
+
 namespace {
 
 bool rope_valid(const hla_rope3d *r, int N, int D) {
@@ -259,6 +262,31 @@ hla_status hla_softmax_anchor(hla_dtype dt, int B, int N, int H, int D, const vo
   a.o = o;
   a.scale = scale;
   a.ws = ws;
+  return launch_anchor(a, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
+}
+
+hla_status hla_softmax_anchor_block_sparse(hla_dtype dt, int B, int N, int H, int D, const void *q, const void *k,
+                                           const void *v, const void *g, float scale, const int *blocks,
+                                           const int *counts, int max_blocks, void *o, void *ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  if (!q || !k || !v || !o || !blocks || !counts) return HLA_ERR_INVALID_ARG;
+  if (!shape_ok(B, N, H) || !isfinite(scale) || !(scale > 0.f) || max_blocks <= 0) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < anchor_workspace_bytes(B, N, H)) return HLA_ERR_WORKSPACE;
+  AnchorArgs a;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.o = o;
+  a.scale = scale;
+  a.ws = ws;
+  a.blocks = blocks;
+  a.counts = counts;
+  a.max_blocks = max_blocks;
   return launch_anchor(a, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
 }
 

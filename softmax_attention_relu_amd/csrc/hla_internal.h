@@ -110,12 +110,17 @@ hipError_t launch_linear_backward(const LinearBwdArgs &a, const LinearPlan &p, h
 LinearPlan plan_linear_causal(int B, int N, int H);
 hipError_t launch_linear_causal(const LinearArgs &a, const LinearPlan &p, hipStream_t stream);
 
+constexpr int kSparseQBlock = 128;  // query rows per block of the block-sparse anchor
+constexpr int kSparseKBlock = 64;   // keys per named block
+
 struct AnchorArgs {
   int B, N, H;
   const void *q, *k, *v, *g;
   void *o;
   float scale;
   void *ws;
+  const int *blocks = nullptr, *counts = nullptr;  // block-sparse form when blocks != nullptr
+  int max_blocks = 0;
 };
 
 size_t anchor_workspace_bytes(int B, int N, int H);

@@ -37,6 +37,7 @@ EXPORTS = (
     "hla_linear_attn_chunked_backward",
     "hla_softmax_anchor_workspace",
     "hla_softmax_anchor",
+    "hla_softmax_anchor_block_sparse",
     "hla_attnres_route",
     "hla_status_string",
 )
@@ -104,6 +105,10 @@ def lib() -> ctypes.CDLL:
         L.hla_softmax_anchor.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_float, c_void_p, c_void_p, c_size_t, c_void_p]
         L.hla_softmax_anchor.restype = c_int
+        L.hla_softmax_anchor_block_sparse.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                                                      c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_int,
+                                                      c_void_p, c_void_p, c_size_t, c_void_p]
+        L.hla_softmax_anchor_block_sparse.restype = c_int
         L.hla_attnres_route.argtypes = [c_int, c_int, c_int, c_int, c_int, POINTER(c_void_p), c_void_p, c_void_p,
                                         c_float, c_void_p, c_void_p, c_void_p]
         L.hla_attnres_route.restype = c_int
@@ -335,6 +340,38 @@ def hla_softmax_anchor(q, k, v, g=None, scale: float | None = None, o=None, ws=N
     st = lib().hla_softmax_anchor(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
                                   _ptr(o), _ptr(ws), nbytes, _stream(stream))
     _check(st, "hla_softmax_anchor")
+    return o
+
+
+SPARSE_Q_BLOCK = 128  # query rows per block of the block-sparse anchor
+SPARSE_K_BLOCK = 64   # keys per named block
+
+
+def hla_softmax_anchor_block_sparse(q, k, v, blocks, counts, g=None, scale: float | None = None, o=None, ws=None,
+                                    stream=None):
+    """Block-sparse gated softmax anchor (bf16); returns o.
+
+    blocks: int32 device tensor (B, H, ceil(N/128), max_blocks) of key-block indices (64 keys each);
+    counts: int32 device tensor (B, H, ceil(N/128)) of entries used per query block.
+    """
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    nqb = -(-N // SPARSE_Q_BLOCK)
+    if blocks.dtype != torch.int32 or counts.dtype != torch.int32:
+        raise TypeError("blocks and counts must be int32")
+    if tuple(blocks.shape[:3]) != (B, H, nqb) or tuple(counts.shape) != (B, H, nqb) or blocks.dim() != 4:
+        raise ValueError("blocks must be (B, H, ceil(N/128), max_blocks) and counts (B, H, ceil(N/128))")
+    if not (blocks.is_contiguous() and counts.is_contiguous()):
+        raise ValueError("blocks and counts must be contiguous")
+    if o is None:
+        o = torch.empty_like(q)
+    ws, nbytes = _workspace(hla_softmax_anchor_workspace(B, N, H, D), q.device, ws)
+    st = lib().hla_softmax_anchor_block_sparse(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                               float(scale), _ptr(blocks), _ptr(counts), int(blocks.shape[3]),
+                                               _ptr(o), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_softmax_anchor_block_sparse")
     return o
 
 

@@ -169,3 +169,34 @@ HYBRID_ANCHOR = AnchorWorkload("hybrid_anchor_bf16_B1H32_N75600_gated", 1, 75600
 HYBRID_ROUTES = [RouteWorkload(f"hybrid_route{i}_bf16_T75600_C2048_S4", 1, 75600, 2048, 4, 44 + i) for i in range(4)]
 CHUNKED_720P60S = LinearWorkload("chunked_bf16_B1H32_241x45x80_L36000", "bf16", 1, 32, (241, 45, 80), False, 5,
                                  chunk_tokens=36000)
+
+
+def block_window_pattern(B: int, H: int, N: int, half_window: int, n_global: int, q_block: int = 128,
+                         k_block: int = 64):
+    """A local-window block pattern for the block-sparse anchor (a stand-in: the pages give none).
+
+    Query block r (rows [r q_block, (r+1) q_block)) names the key blocks whose
+    index lies within ``half_window`` of the key block holding the query
+    block's first row, plus the first ``n_global`` key blocks; the same for
+    every (b, h), each list ascending and without repeats. Returns int32
+    arrays blocks (B, H, nqb, max_blocks), padded with -1, and counts (B, H, nqb).
+    """
+    nqb, nkb = -(-N // q_block), -(-N // k_block)
+    lists = []
+    for r in range(nqb):
+        c = (r * q_block) // k_block
+        named = set(range(max(0, c - half_window), min(nkb, c + half_window + 1))) | set(range(min(n_global, nkb)))
+        lists.append(sorted(named))
+    width = max(len(x) for x in lists)
+    blocks = np.full((B, H, nqb, width), -1, dtype=np.int32)
+    counts = np.zeros((B, H, nqb), dtype=np.int32)
+    for r, x in enumerate(lists):
+        blocks[:, :, r, :len(x)] = x
+        counts[:, :, r] = len(x)
+    return blocks, counts
+
+
+# Block-sparse anchor at 720p/5s: a window of +-72 key blocks (about +-1.3
+# latent frames of 3 600 tokens) plus 4 global blocks, ~12% of the pairs.
+SPARSE_ANCHOR_720P5S = AnchorWorkload("sparse_anchor_bf16_B1H32_N75600_window72_global4_gated", 1, 75600, 32, 48)
+SPARSE_ANCHOR_WINDOW = (72, 4)

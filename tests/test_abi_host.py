@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     assert sorted(hla.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -197,6 +197,26 @@ def test_anchor_validation(L):
     assert call(D=32) == E.HLA_ERR_UNSUPPORTED
     assert call(ws=None) == E.HLA_ERR_WORKSPACE
     assert call(ws_bytes=64 * 64 * 2 - 1) == E.HLA_ERR_WORKSPACE
+
+
+def test_sparse_anchor_validation(L):
+    E = hla
+
+    def call(dt=0, N=8, D=64, scale=0.125, blocks=FAKE, counts=FAKE, max_blocks=4, ws_bytes=1 << 40):
+        return L.hla_softmax_anchor_block_sparse(dt, 1, N, 1, D, FAKE, FAKE, FAKE, None, scale, blocks, counts,
+                                                 max_blocks, FAKE, FAKE, ws_bytes, None)
+
+    assert call(blocks=None) == E.HLA_ERR_INVALID_ARG
+    assert call(counts=None) == E.HLA_ERR_INVALID_ARG
+    assert call(max_blocks=0) == E.HLA_ERR_INVALID_ARG
+    assert call(scale=0.0) == E.HLA_ERR_INVALID_ARG
+    assert call(N=0) == E.HLA_ERR_INVALID_ARG
+    assert call(dt=1) == E.HLA_ERR_UNSUPPORTED
+    assert call(D=32) == E.HLA_ERR_UNSUPPORTED
+    assert call(ws_bytes=64 * 64 * 2 - 1) == E.HLA_ERR_WORKSPACE
+    src = open(os.path.join(ROOT, "include", "hla.h")).read()
+    assert "#define HLA_SPARSE_Q_BLOCK 128" in src and hla.SPARSE_Q_BLOCK == 128
+    assert "#define HLA_SPARSE_K_BLOCK 64" in src and hla.SPARSE_K_BLOCK == 64
 
 
 def test_route_validation(L):
