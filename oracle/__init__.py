@@ -26,6 +26,8 @@ pages' order of operations:
                      3.4, causal equation and Algorithm 1).
 * ``softmax_anchor`` -- gated non-causal softmax attention (SANA-Video 2.0
                      abstract and summary, hybrid 3:1 design).
+* ``softmax_anchor_backward`` -- gradients of the gated anchor, derived by
+                     hand from its definition.
 * ``softmax_anchor_block_sparse`` -- the anchor restricted to caller-given
                      key blocks per query block (the pages name a sparse
                      anchor without its pattern: parity unpinned against them).
@@ -41,7 +43,7 @@ RoPE pairing and frequency convention (the pages do not define
 from .rope3d import Rope3D, rope3d_angles, rope3d_rotate
 from .linear_attention import (linear_attention, linear_attention_backward, linear_attention_causal,
                                linear_attention_chunked, linear_attention_chunked_backward)
-from .softmax_anchor import softmax_anchor, softmax_anchor_block_sparse
+from .softmax_anchor import softmax_anchor, softmax_anchor_backward, softmax_anchor_block_sparse
 from .attnres_router import attnres_route
 
 __all__ = [
@@ -55,5 +57,6 @@ __all__ = [
     "linear_attention_chunked_backward",
     "softmax_anchor",
     "softmax_anchor_block_sparse",
+    "softmax_anchor_backward",
     "attnres_route",
 ]

@@ -100,3 +100,50 @@ def softmax_anchor_block_sparse(q, k, v, blocks, counts, g=None, scale: float | 
     if g is not None:
         out = _sigmoid(np.asarray(g, dtype=np.float64)[:, rows]) * out
     return out
+
+
+def softmax_anchor_backward(q, k, v, do, g=None, scale: float | None = None, row_block: int = 256):
+    """Gradients of the gated softmax anchor, fp64.
+
+    Differentiates the definition at the top of this module by hand. With
+    s_i = sigmoid(g_i) (1 without a gate), y_i = sum_j p_ij v_j and the
+    upstream gradient dO:
+
+        dG_i   = dO_i * y_i * s_i * (1 - s_i),   dY_i = dO_i * s_i
+        dP_ij  = dY_i . v_j,                     Delta_i = dY_i . y_i = sum_j p_ij dP_ij
+        dL_ij  = p_ij (dP_ij - Delta_i)          (gradient of the logit l_ij)
+        dq_i   = scale sum_j dL_ij k_j,  dk_j = scale sum_i dL_ij q_i,  dv_j = sum_i p_ij dY_i
+
+    Query rows are taken ``row_block`` at a time; the key-side sums add the
+    blocks in order. Returns (dq, dk, dv, dg); dg is None without a gate.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, N, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    s = np.ones_like(q) if g is None else _sigmoid(np.asarray(g, dtype=np.float64))
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dg = None if g is None else np.zeros_like(q)
+    for b in range(B):
+        for h in range(H):
+            kh, vh = k[b, :, h, :], v[b, :, h, :]
+            for r0 in range(0, N, row_block):
+                rr = slice(r0, min(N, r0 + row_block))
+                logits = scale * (q[b, rr, h, :] @ kh.T)
+                p = np.exp(logits - logits.max(axis=1, keepdims=True))
+                p = p / p.sum(axis=1, keepdims=True)
+                y = p @ vh
+                sh = s[b, rr, h, :]
+                if g is not None:
+                    dg[b, rr, h, :] = do[b, rr, h, :] * y * sh * (1.0 - sh)
+                dy = do[b, rr, h, :] * sh
+                dp = dy @ vh.T
+                delta = np.sum(dy * y, axis=1, keepdims=True)
+                dl = p * (dp - delta)
+                dq[b, rr, h, :] = scale * (dl @ kh)
+                dk[b, :, h, :] += scale * (dl.T @ q[b, rr, h, :])
+                dv[b, :, h, :] += p.T @ dy
+    return dq, dk, dv, dg

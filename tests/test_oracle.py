@@ -577,6 +577,48 @@ def test_anchor_matches_torch_sdpa_f64():
     np.testing.assert_allclose(got, ref.numpy().transpose(0, 2, 1, 3), rtol=1e-11, atol=1e-13)
 
 
+@pytest.mark.parametrize("gated", [True, False])
+def test_anchor_backward_matches_autograd(gated):
+    """Hand-derived anchor gradients against torch autograd of an independently written forward
+    (softmax over the key axis, sigmoid gate), fp64 on the CPU; row blocks smaller than N so the
+    key-side sums run over several blocks."""
+    B, N, H, D = 2, 40, 2, 16
+    q, k, v, g, do = (_randn(B, N, H, D) for _ in range(5))
+    ts = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, g)]
+    att = torch.softmax(torch.einsum("bihd,bjhd->bhij", ts[0], ts[1]) * 0.3, dim=-1)
+    out = torch.einsum("bhij,bjhd->bihd", att, ts[2])
+    if gated:
+        out = torch.sigmoid(ts[3]) * out
+    out.backward(torch.tensor(do))
+    got = oracle.softmax_anchor_backward(q, k, v, do, g if gated else None, scale=0.3, row_block=16)
+    for x, t in zip(got[:3], ts[:3]):
+        np.testing.assert_allclose(x, t.grad.numpy(), rtol=1e-9, atol=1e-12)
+    if gated:
+        np.testing.assert_allclose(got[3], ts[3].grad.numpy(), rtol=1e-9, atol=1e-12)
+    else:
+        assert got[3] is None
+
+
+def test_anchor_backward_matches_finite_differences():
+    """Central differences of the forward anchor oracle (loss sum(dO * o)) on a tiny case."""
+    B, N, H, D = 1, 5, 1, 4
+    q, k, v, g, do = (_randn(B, N, H, D) for _ in range(5))
+    grads = oracle.softmax_anchor_backward(q, k, v, do, g, scale=0.7, row_block=2)
+
+    def loss(q_, k_, v_, g_):
+        return float(np.sum(do * oracle.softmax_anchor(q_, k_, v_, g_, scale=0.7)))
+
+    h = 1e-6
+    for which, grad in enumerate(grads):
+        for idx in np.ndindex(q.shape):
+            xs = [q.copy(), k.copy(), v.copy(), g.copy()]
+            xs[which][idx] += h
+            up = loss(*xs)
+            xs[which][idx] -= 2 * h
+            dn = loss(*xs)
+            assert abs((up - dn) / (2 * h) - grad[idx]) <= 1e-6 * (1.0 + abs(grad[idx])), (which, idx)
+
+
 def test_sparse_anchor_matches_python_loops():
     """Tiny block-sparse case against loops over the allowed keys (query blocks of 4, key blocks of 3)."""
     B, N, H, D = 1, 10, 2, 4

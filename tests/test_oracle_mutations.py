@@ -63,6 +63,10 @@ MUTATIONS = [
     # anchor: missing scale, softmax over the wrong axis
     ("softmax_anchor.py", "logits = scale * (q[b, rr, h, :] @ kh.T)", "logits = (q[b, rr, h, :] @ kh.T)"),
     ("softmax_anchor.py", "p = p / p.sum(axis=1, keepdims=True)", "p = p / p.sum(axis=0, keepdims=True)"),
+    # anchor backward: Delta dropped, key gradient unscaled, value gradient from dO instead of dY
+    ("softmax_anchor.py", "dl = p * (dp - delta)", "dl = p * dp"),
+    ("softmax_anchor.py", "dk[b, :, h, :] += scale * (dl.T @ q[b, rr, h, :])", "dk[b, :, h, :] += dl.T @ q[b, rr, h, :]"),
+    ("softmax_anchor.py", "dv[b, :, h, :] += p.T @ dy", "dv[b, :, h, :] += p.T @ do[b, rr, h, :]"),
     # block-sparse anchor: last key of a block dropped, query block taken with the key block size
     ("softmax_anchor.py", "range(m * k_block, min(N, (m + 1) * k_block))", "range(m * k_block, min(N, (m + 1) * k_block - 1))"),
     ("softmax_anchor.py", "                r = i // q_block", "                r = i // k_block"),
