@@ -360,6 +360,39 @@ def main() -> int:
         log(f"[bench] backward 720p/5s: {bw_ms:.3f} ms")
         del bws, bouts, bdo
 
+    # ---------------- anchor backward leg: gradients of the 720p/5s anchor (gated)
+    if not args.no_legs:
+        ado = dev(synth.randn(aw.seed, (aw.B, aw.N, aw.H, aw.D), stream=4))
+        aws = torch.empty(hla.hla_softmax_anchor_backward_workspace(aw.B, aw.N, aw.H, aw.D), dtype=torch.uint8,
+                          device="cuda")
+        agrads = [torch.empty_like(anc["q"]) for _ in range(4)]
+
+        def abwd_call():
+            hla.hla_softmax_anchor_backward(anc["q"], anc["k"], anc["v"], ado, anc["g"], aw.scale, *agrads, ws=aws)
+
+        abwd_call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(2):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            abwd_call()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        ab_ms = float(np.mean(times))
+        # algorithmic: the five N x N products of the gradient (S, dP, dV, dK, dQ), 10 N^2 D per head; the
+        # schedule recomputes the forward (4) and S, dP in both gradient kernels: 18 N^2 D
+        ab_alg = 10.0 * aw.B * aw.H * float(aw.N) ** 2 * aw.D
+        ab_sched = 18.0 * aw.B * aw.H * float(aw.N) ** 2 * aw.D
+        out.setdefault("legs", {})["anchor_backward_720p5s"] = {
+            "N": aw.N, "ms": ab_ms, "algorithmic_flop": ab_alg, "schedule_flop": ab_sched,
+            "algorithmic_tflops": ab_alg / (ab_ms * 1e-3) / 1e12,
+            "mfma_frac": ab_alg / (ab_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "schedule_tflops": ab_sched / (ab_ms * 1e-3) / 1e12}
+        log(f"[bench] anchor backward 720p/5s: {ab_ms:.1f} ms")
+        del ado, aws, agrads
+
     # ---------------- block-sparse anchor leg: 720p/5s with a local-window pattern
     if not args.no_legs:
         sw = synth.SPARSE_ANCHOR_720P5S

@@ -18,6 +18,8 @@
  *                            full-rank anchor layer).
  *   hla_softmax_anchor_block_sparse
  *                            the anchor restricted to caller-given key blocks.
+ *   hla_softmax_anchor_backward
+ *                            gradients of the anchor.
  *   hla_attnres_route        block attention-residual (AttnRes) depth router.
  *
  * Conventions shared by every entry point
@@ -236,6 +238,30 @@ size_t hla_softmax_anchor_workspace(int B, int N, int H, int D);
 hla_status hla_softmax_anchor(hla_dtype dt, int B, int N, int H, int D,
                               const void *q, const void *k, const void *v, const void *g,
                               float scale, void *o, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gradients of hla_softmax_anchor (bf16). Given the forward's inputs and dO, the
+ * gradient of a scalar loss with respect to o, it writes dq, dk, dv and dg (the
+ * latter when g is given). With p_ij the softmax weights, y_i = sum_j p_ij v_j
+ * the ungated output and s = sigmoid(g) (1 without a gate):
+ *   dg_i = dO_i y_i s_i (1 - s_i),  dY_i = dO_i s_i,  dP_ij = dY_i . v_j
+ *   Delta_i = dY_i . y_i,  dL_ij = p_ij (dP_ij - Delta_i)
+ *   dq_i = scale sum_j dL_ij k_j,  dk_j = scale sum_i dL_ij q_i,  dv_j = sum_i p_ij dY_i
+ * The forward is recomputed (a pass that also yields each row's normaliser),
+ * nothing of it is kept. q, k, v, g, dO, dq, dk, dv, dg: [B][N][H][D] bf16;
+ * dg must be given exactly when g is. Products run on bf16 matrix cores with
+ * float accumulation; p, dL and dY are rounded to bf16 as product operands.
+ * No atomics: repeated calls are bitwise identical.
+ * ws: at least hla_softmax_anchor_backward_workspace(B, N, H, D) bytes.
+ * Errors: as hla_softmax_anchor, plus INVALID_ARG for null dO/dq/dk/dv or a
+ * gate given without dg (or dg without g).
+ */
+size_t hla_softmax_anchor_backward_workspace(int B, int N, int H, int D);
+hla_status hla_softmax_anchor_backward(hla_dtype dt, int B, int N, int H, int D,
+                                       const void *q, const void *k, const void *v, const void *g,
+                                       float scale, const void *dO,
+                                       void *dq, void *dk, void *dv, void *dg,
+                                       void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Block-sparse form of hla_softmax_anchor. The pages name a sparse anchor

@@ -27,6 +27,8 @@
 // tile exceeds it by more than 8 (log2 units), so exponentials stay <= 2^8
 // and the O / row-sum rescale is almost never taken. The normaliser uses the
 // same reference max, so the result is exact up to rounding.
+#include <string.h>
+
 #include "device_common.h"
 
 namespace hla {
@@ -105,6 +107,11 @@ struct FwdArgs {
   // block-sparse form: key tiles named per (b*H + h, query block), [..][max_blocks]
   const int *blocks, *counts;
   int n_qb, max_blocks;
+  // gradient preparation (kPrep): reads dO, writes dG, dY = dO * sigmoid(g) (bf16,
+  // the layout of q) and per row the log2-domain normaliser and Delta = dY . y
+  const uint16_t *dO;
+  uint16_t *dg, *dy;
+  float *lse, *delta;  // [B*H][N]
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -113,8 +120,11 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // instruction): the normaliser uses the same weights as the P.V product.
 // kSparse: the work-group's query rows form one query block and visit only
 // the 64-key tiles named for it (entries outside the key range are skipped);
-// otherwise every tile in order.
-template <int WAVES, int MINW, bool kSparse>
+// otherwise every tile in order. kPrep: the epilogue writes the inputs of the
+// gradient kernels instead of o (y = the ungated output, s = sigmoid(g)):
+// dG = dO y s (1 - s), dY = dO s (bf16), Delta = dY . y and L = mref + log2(rowsum),
+// so that p_ij = exp2(c s_ij - L_i) are the normalised weights.
+template <int WAVES, int MINW, bool kSparse, bool kPrep>
 __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a) {
   constexpr int kThreads = 64 * WAVES;
   // 16-byte chunks of K (and of V^T) per thread per tile: 512 chunks each
@@ -306,6 +316,49 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
   const int n = q0 + tl;
   const float l = lsum + __shfl_xor(lsum, 32);
   const float inv = l > 0.f ? 1.f / l : 0.f;  // no key visited: the output is 0
+  if constexpr (kPrep) {
+    const size_t row = head_base + (size_t)min(n, a.N - 1) * tok_stride;
+    float part = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t off = row + 32 * mb + 8 * i + 4 * half;
+        const uint2 ow = *reinterpret_cast<const uint2 *>(a.dO + off);
+        const float dov[4] = {bf16_lo(ow.x), bf16_hi(ow.x), bf16_lo(ow.y), bf16_hi(ow.y)};
+        float gv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (a.g) {
+          const uint2 gw = *reinterpret_cast<const uint2 *>(a.g + off);
+          gv[0] = bf16_lo(gw.x); gv[1] = bf16_hi(gw.x); gv[2] = bf16_lo(gw.y); gv[3] = bf16_hi(gw.y);
+        }
+        float dgv[4], dyv[4], y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[j] = oacc[mb][4 * i + j] * inv;
+          const float sg = a.g ? __builtin_amdgcn_rcpf(1.f + __expf(-gv[j])) : 1.f;
+          dgv[j] = dov[j] * y[j] * sg * (1.f - sg);
+          dyv[j] = dov[j] * sg;
+        }
+        // Delta from the bf16 dY the dP product reads, so that sum_j dS_ij = 0
+        // holds for the kernels' own dP (exactly zero gradients stay near zero)
+        const uint2 dyw = make_uint2(pack_bf16(dyv[0], dyv[1]), pack_bf16(dyv[2], dyv[3]));
+        part += bf16_lo(dyw.x) * y[0] + bf16_hi(dyw.x) * y[1] + bf16_lo(dyw.y) * y[2] + bf16_hi(dyw.y) * y[3];
+        if (n < a.N) {
+          *reinterpret_cast<uint2 *>(a.dy + off) = dyw;
+          if (a.g)
+            *reinterpret_cast<uint2 *>(a.dg + off) =
+                make_uint2(pack_bf16(dgv[0], dgv[1]), pack_bf16(dgv[2], dgv[3]));
+        }
+      }
+    const float delta = part + __shfl_xor(part, 32);
+    if (n < a.N) {
+      if (half == 0) {
+        a.lse[(size_t)bh * a.N + n] = mref + log2f(l);
+        a.delta[(size_t)bh * a.N + n] = delta;
+      }
+    }
+    return;
+  }
   if (n < a.N) {
     const size_t row = head_base + (size_t)n * tok_stride;
 #pragma unroll
@@ -328,7 +381,384 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Gradients. With p_ij = exp2(c s_ij - L_i) (L from the preparation pass),
+// dP_ij = dY_i . v_j and dS_ij = p_ij (dP_ij - Delta_i), the gradient of the
+// logit: dq_i = scale sum_j dS_ij k_j, dk_j = scale sum_i dS_ij q_i and
+// dv_j = sum_i p_ij dY_i. Two kernels, no atomics: one owns keys and walks the
+// query tiles (dk, dv), the other owns queries and walks the key tiles (dq).
+// Both reuse the forward's layout: the scores come out with each lane holding
+// one column token and 32 row tokens, which feed the next products as B
+// operands straight from registers against transposed tiles whose tokens are
+// permuted in groups of 16 (the V^T layout of anchor_vt).
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *dy;  // [B][N][H][64]
+  const uint16_t *qt, *dyt, *kt;   // [B*H][64][npad], tokens permuted in groups of 16
+  const float *lse, *delta;        // [B*H][N]
+  uint16_t *dq, *dk, *dv;
+  int N, H, npad;
+  float c, scale;
+};
+
+// B operands of 32 tokens' rows: lane (tl, half) holds token n (its wave's
+// token tl), dims 16 s + 8 half .. +7 (zero past N)
+__device__ __forceinline__ void row_operands(const uint16_t *base, size_t stride, int n, int half, int N,
+                                             bf16x8_t x[4]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (n < N) w = *reinterpret_cast<const uint4 *>(base + (size_t)n * stride + 16 * s + 8 * half);
+    x[s] = __builtin_bit_cast(bf16x8_t, w);
+  }
+}
+
+// f * acc rounded to bf16; the lane holds column token n, dims 32 mb + 8 i + 4 half + j
+__device__ __forceinline__ void store_cols(uint16_t *base, size_t stride, int n, int half, const f32x16_t acc[2],
+                                           float f) {
+  const size_t row = (size_t)n * stride;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x16_t &x = acc[mb];
+      *reinterpret_cast<uint2 *>(base + row + 32 * mb + 8 * i + 4 * half) =
+          make_uint2(pack_bf16(f * x[4 * i], f * x[4 * i + 1]), pack_bf16(f * x[4 * i + 2], f * x[4 * i + 3]));
+    }
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 2) void anchor_dkdv_kernel(BwdArgs a) {
+  static_assert(64 * WAVES == kBK * 8, "one 16-byte chunk of each tile per thread");
+  __shared__ __align__(16) uint16_t qs[2][kBK * kKRow];  // Q rows of the query tile
+  __shared__ __align__(16) uint16_t ds[2][kBK * kKRow];  // dY rows
+  __shared__ __align__(16) uint16_t qts[2][kD * kVRow];  // Q^T, permuted
+  __shared__ __align__(16) uint16_t dts[2][kD * kVRow];  // dY^T, permuted
+  __shared__ __align__(16) float ls[2][kBK], dls[2][kBK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, tl = lane & 31;
+  const int bh = blockIdx.y;
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int k0 = blockIdx.x * (32 * WAVES) + wave * 32;
+  const size_t tok_stride = (size_t)a.H * kD;
+  const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD;
+
+  bf16x8_t kb[4], vb[4];
+  row_operands(a.k + head_base, tok_stride, k0 + tl, half, a.N, kb);
+  row_operands(a.v + head_base, tok_stride, k0 + tl, half, a.N, vb);
+  const uint16_t *qp = a.q + head_base, *dp = a.dy + head_base;
+  const uint16_t *qtp = a.qt + (size_t)bh * kD * a.npad, *dtp = a.dyt + (size_t)bh * kD * a.npad;
+  const float *lsp = a.lse + (size_t)bh * a.N, *dlp = a.delta + (size_t)bh * a.N;
+
+  const int row = tid >> 3, ch = tid & 7;
+  uint4 sreg[4];
+  float sf = 0.f;
+  auto load_tile = [&](int t) {
+    const int n0 = t * kBK, n = n0 + row;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    sreg[0] = n < a.N ? *reinterpret_cast<const uint4 *>(qp + (size_t)n * tok_stride + 8 * ch) : z;
+    sreg[1] = n < a.N ? *reinterpret_cast<const uint4 *>(dp + (size_t)n * tok_stride + 8 * ch) : z;
+    sreg[2] = *reinterpret_cast<const uint4 *>(qtp + (size_t)row * a.npad + n0 + 8 * ch);
+    sreg[3] = *reinterpret_cast<const uint4 *>(dtp + (size_t)row * a.npad + n0 + 8 * ch);
+    if (tid < 2 * kBK) {
+      const int qn = n0 + (tid & (kBK - 1));
+      // past N: a weight of exactly 0 and no Delta
+      sf = tid < kBK ? (qn < a.N ? lsp[qn] : INFINITY) : (qn < a.N ? dlp[qn] : 0.f);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    *reinterpret_cast<uint4 *>(&qs[buf][row * kKRow + 8 * ch]) = sreg[0];
+    *reinterpret_cast<uint4 *>(&ds[buf][row * kKRow + 8 * ch]) = sreg[1];
+    *reinterpret_cast<uint4 *>(&qts[buf][row * kVRow + 8 * ch]) = sreg[2];
+    *reinterpret_cast<uint4 *>(&dts[buf][row * kVRow + 8 * ch]) = sreg[3];
+    if (tid < 2 * kBK) (tid < kBK ? ls : dls)[buf][tid & (kBK - 1)] = sf;
+  };
+
+  f32x16_t dva[2], dka[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dva[mb][i] = dka[mb][i] = 0.f;
+
+  const int ntiles = (a.N + kBK - 1) / kBK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    // scores and dP of the tile's 64 queries (rows) against the wave's 32 keys
+    f32x16_t sacc[2], pacc[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[qb][i] = pacc[qb][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int off = (32 * qb + tl) * kKRow + 16 * s + 8 * half;
+        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&qs[buf][off]), kb[s],
+                                                           sacc[qb], 0, 0, 0);
+        pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&ds[buf][off]), vb[s],
+                                                           pacc[qb], 0, 0, 0);
+      }
+    }
+    // weights and logit gradients: lane rows 32 qb + 8 i + 4 half + j
+    bf16x8_t pw[2][2], sw[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float pv[16], dv[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4_t L = *reinterpret_cast<const f32x4_t *>(&ls[buf][32 * qb + 8 * i + 4 * half]);
+        const f32x4_t Dl = *reinterpret_cast<const f32x4_t *>(&dls[buf][32 * qb + 8 * i + 4 * half]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pj = __builtin_amdgcn_exp2f(fmaf(sacc[qb][4 * i + j], a.c, -L[j]));
+          pv[4 * i + j] = pj;
+          dv[4 * i + j] = pj * (pacc[qb][4 * i + j] - Dl[j]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        pw[qb][u] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pack_bf16(pv[8 * u], pv[8 * u + 1]), pack_bf16(pv[8 * u + 2], pv[8 * u + 3]),
+                                 pack_bf16(pv[8 * u + 4], pv[8 * u + 5]), pack_bf16(pv[8 * u + 6], pv[8 * u + 7])));
+        sw[qb][u] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pack_bf16(dv[8 * u], dv[8 * u + 1]), pack_bf16(dv[8 * u + 2], dv[8 * u + 3]),
+                                 pack_bf16(dv[8 * u + 4], dv[8 * u + 5]), pack_bf16(dv[8 * u + 6], dv[8 * u + 7])));
+      }
+    }
+    // dV^T += dY^T P and dK^T += Q^T dS over the tile's queries
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int off = (32 * mb + tl) * kVRow + 32 * qb + 16 * u + 8 * half;
+          dva[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&dts[buf][off]),
+                                                            pw[qb][u], dva[mb], 0, 0, 0);
+          dka[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&qts[buf][off]),
+                                                            sw[qb][u], dka[mb], 0, 0, 0);
+        }
+    if (t + 1 < ntiles) {
+      store_tile(buf ^ 1);  // the other buffer was last read two tiles ago
+      __syncthreads();
+    }
+  }
+  const int n = k0 + tl;
+  if (n < a.N) {
+    store_cols(a.dk + head_base, tok_stride, n, half, dka, a.scale);
+    store_cols(a.dv + head_base, tok_stride, n, half, dva, 1.f);
+  }
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 2) void anchor_dq_kernel(BwdArgs a) {
+  static_assert(64 * WAVES == kBK * 8, "one 16-byte chunk of each tile per thread");
+  __shared__ __align__(16) uint16_t ks[2][kBK * kKRow];   // K rows of the key tile
+  __shared__ __align__(16) uint16_t vr[2][kBK * kKRow];   // V rows
+  __shared__ __align__(16) uint16_t kts[2][kD * kVRow];  // K^T, permuted
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, tl = lane & 31;
+  const int bh = blockIdx.y;
+  const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const int q0 = blockIdx.x * (32 * WAVES) + wave * 32;
+  const size_t tok_stride = (size_t)a.H * kD;
+  const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD;
+
+  bf16x8_t qb[4], db[4];
+  row_operands(a.q + head_base, tok_stride, q0 + tl, half, a.N, qb);
+  row_operands(a.dy + head_base, tok_stride, q0 + tl, half, a.N, db);
+  const int nq = min(q0 + tl, a.N - 1);
+  const float L = a.lse[(size_t)bh * a.N + nq], Dl = a.delta[(size_t)bh * a.N + nq];
+  const uint16_t *kp = a.k + head_base, *vp = a.v + head_base;
+  const uint16_t *ktp = a.kt + (size_t)bh * kD * a.npad;
+
+  const int row = tid >> 3, ch = tid & 7;
+  uint4 sreg[3];
+  auto load_tile = [&](int t) {
+    const int n0 = t * kBK, n = n0 + row;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    sreg[0] = n < a.N ? *reinterpret_cast<const uint4 *>(kp + (size_t)n * tok_stride + 8 * ch) : z;
+    sreg[1] = n < a.N ? *reinterpret_cast<const uint4 *>(vp + (size_t)n * tok_stride + 8 * ch) : z;
+    sreg[2] = *reinterpret_cast<const uint4 *>(ktp + (size_t)row * a.npad + n0 + 8 * ch);
+  };
+  auto store_tile = [&](int buf) {
+    *reinterpret_cast<uint4 *>(&ks[buf][row * kKRow + 8 * ch]) = sreg[0];
+    *reinterpret_cast<uint4 *>(&vr[buf][row * kKRow + 8 * ch]) = sreg[1];
+    *reinterpret_cast<uint4 *>(&kts[buf][row * kVRow + 8 * ch]) = sreg[2];
+  };
+
+  f32x16_t dqa[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqa[mb][i] = 0.f;
+
+  const int ntiles = (a.N + kBK - 1) / kBK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    // S^T and dP^T of the tile's 64 keys (rows) against the wave's 32 queries
+    f32x16_t sacc[2], pacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = pacc[kb][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int off = (32 * kb + tl) * kKRow + 16 * s + 8 * half;
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&ks[buf][off]), qb[s],
+                                                           sacc[kb], 0, 0, 0);
+        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&vr[buf][off]), db[s],
+                                                           pacc[kb], 0, 0, 0);
+      }
+    }
+    const bool tail = (t + 1) * kBK > a.N;
+    bf16x8_t sw[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float dv[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * i + j;
+          float pj = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], a.c, -L));
+          if (tail && t * kBK + 32 * kb + 8 * i + 4 * half + j >= a.N) pj = 0.f;
+          dv[e] = pj * (pacc[kb][e] - Dl);
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        sw[kb][u] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pack_bf16(dv[8 * u], dv[8 * u + 1]), pack_bf16(dv[8 * u + 2], dv[8 * u + 3]),
+                                 pack_bf16(dv[8 * u + 4], dv[8 * u + 5]), pack_bf16(dv[8 * u + 6], dv[8 * u + 7])));
+    }
+    // dQ^T += K^T dS^T over the tile's keys
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int off = (32 * mb + tl) * kVRow + 32 * kb + 16 * u + 8 * half;
+          dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&kts[buf][off]),
+                                                            sw[kb][u], dqa[mb], 0, 0, 0);
+        }
+    if (t + 1 < ntiles) {
+      store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  const int n = q0 + tl;
+  if (n < a.N) store_cols(a.dq + head_base, tok_stride, n, half, dqa, a.scale);
+}
+
+hipError_t launch_vt(const void *x, void *xt, int B, int N, int H, int npad, hipStream_t stream) {
+  VtArgs va;
+  va.v = reinterpret_cast<const uint16_t *>(x);
+  va.vt = reinterpret_cast<uint16_t *>(xt);
+  va.N = N;
+  va.H = H;
+  va.npad = npad;
+  hipLaunchKernelGGL(anchor_vt_kernel, dim3(npad / kBK, B * H), dim3(256), 0, stream, va);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+namespace {
+// gradient workspace: V^T, Q^T, dY^T, K^T (bf16, [B*H][64][npad]), dY (bf16, the
+// layout of q), L and Delta (fp32, [B*H][N])
+struct BwdLayout {
+  size_t vt, qt, dyt, kt, dy, lse, delta, total;
+};
+BwdLayout bwd_layout(int B, int N, int H) {
+  const size_t npad = ((size_t)N + kBK - 1) / kBK * kBK;
+  const size_t t = align256((size_t)B * H * kD * npad * sizeof(uint16_t));
+  BwdLayout l;
+  l.vt = 0;
+  l.qt = t;
+  l.dyt = 2 * t;
+  l.kt = 3 * t;
+  l.dy = 4 * t;
+  l.lse = l.dy + align256((size_t)B * N * H * kD * sizeof(uint16_t));
+  l.delta = l.lse + align256((size_t)B * H * N * sizeof(float));
+  l.total = l.delta + align256((size_t)B * H * N * sizeof(float));
+  return l;
+}
+}  // namespace
+
+size_t anchor_backward_workspace_bytes(int B, int N, int H) { return bwd_layout(B, N, H).total; }
+
+hipError_t launch_anchor_backward(const AnchorBwdArgs &a, hipStream_t stream) {
+  const int heads = a.B * a.H;
+  const int npad = (a.N + kBK - 1) / kBK * kBK;
+  const BwdLayout l = bwd_layout(a.B, a.N, a.H);
+  char *ws = reinterpret_cast<char *>(a.ws);
+  uint16_t *vt = reinterpret_cast<uint16_t *>(ws + l.vt), *qt = reinterpret_cast<uint16_t *>(ws + l.qt);
+  uint16_t *dyt = reinterpret_cast<uint16_t *>(ws + l.dyt), *kt = reinterpret_cast<uint16_t *>(ws + l.kt);
+  uint16_t *dy = reinterpret_cast<uint16_t *>(ws + l.dy);
+  float *lse = reinterpret_cast<float *>(ws + l.lse), *delta = reinterpret_cast<float *>(ws + l.delta);
+
+  hipError_t e = launch_vt(a.v, vt, a.B, a.N, a.H, npad, stream);
+  if (e != hipSuccess) return e;
+  // preparation: the forward with its epilogue writing dG, dY, L, Delta
+  FwdArgs fa;
+  memset(&fa, 0, sizeof(fa));
+  fa.q = reinterpret_cast<const uint16_t *>(a.q);
+  fa.k = reinterpret_cast<const uint16_t *>(a.k);
+  fa.g = reinterpret_cast<const uint16_t *>(a.g);
+  fa.vt = vt;
+  fa.N = a.N;
+  fa.H = a.H;
+  fa.npad = npad;
+  fa.c = a.scale * 1.4426950408889634f;
+  fa.dO = reinterpret_cast<const uint16_t *>(a.dO);
+  fa.dg = reinterpret_cast<uint16_t *>(a.dg);
+  fa.dy = dy;
+  fa.lse = lse;
+  fa.delta = delta;
+  hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, false, true>),
+                     dim3((a.N + 32 * kWaves - 1) / (32 * kWaves), heads), dim3(64 * kWaves), 0, stream, fa);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = launch_vt(a.q, qt, a.B, a.N, a.H, npad, stream)) != hipSuccess) return e;
+  if ((e = launch_vt(dy, dyt, a.B, a.N, a.H, npad, stream)) != hipSuccess) return e;
+  if ((e = launch_vt(a.k, kt, a.B, a.N, a.H, npad, stream)) != hipSuccess) return e;
+
+  BwdArgs ba;
+  ba.q = reinterpret_cast<const uint16_t *>(a.q);
+  ba.k = reinterpret_cast<const uint16_t *>(a.k);
+  ba.v = reinterpret_cast<const uint16_t *>(a.v);
+  ba.dy = dy;
+  ba.qt = qt;
+  ba.dyt = dyt;
+  ba.kt = kt;
+  ba.lse = lse;
+  ba.delta = delta;
+  ba.dq = reinterpret_cast<uint16_t *>(a.dq);
+  ba.dk = reinterpret_cast<uint16_t *>(a.dk);
+  ba.dv = reinterpret_cast<uint16_t *>(a.dv);
+  ba.N = a.N;
+  ba.H = a.H;
+  ba.npad = npad;
+  ba.c = fa.c;
+  ba.scale = a.scale;
+  constexpr int kBwdWaves = 8;
+  const dim3 grid((a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves), heads);
+  hipLaunchKernelGGL((anchor_dkdv_kernel<kBwdWaves>), grid, dim3(64 * kBwdWaves), 0, stream, ba);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((anchor_dq_kernel<kBwdWaves>), grid, dim3(64 * kBwdWaves), 0, stream, ba);
+  return hipGetLastError();
+}
 
 size_t anchor_workspace_bytes(int B, int N, int H) {
   const size_t npad = ((size_t)N + kBK - 1) / kBK * kBK;
@@ -338,21 +768,14 @@ size_t anchor_workspace_bytes(int B, int N, int H) {
 hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   const int heads = a.B * a.H;
   const int npad = (a.N + kBK - 1) / kBK * kBK;
-  VtArgs va;
-  va.v = reinterpret_cast<const uint16_t *>(a.v);
-  va.vt = reinterpret_cast<uint16_t *>(a.ws);
-  va.N = a.N;
-  va.H = a.H;
-  va.npad = npad;
-  hipLaunchKernelGGL(anchor_vt_kernel, dim3(npad / kBK, heads), dim3(256), 0, stream, va);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_vt(a.v, a.ws, a.B, a.N, a.H, npad, stream);
   if (e != hipSuccess) return e;
 
   FwdArgs fa;
   fa.q = reinterpret_cast<const uint16_t *>(a.q);
   fa.k = reinterpret_cast<const uint16_t *>(a.k);
   fa.g = reinterpret_cast<const uint16_t *>(a.g);
-  fa.vt = va.vt;
+  fa.vt = reinterpret_cast<const uint16_t *>(a.ws);
   fa.o = reinterpret_cast<uint16_t *>(a.o);
   fa.N = a.N;
   fa.H = a.H;
@@ -363,11 +786,11 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   fa.max_blocks = a.max_blocks;
   if (a.blocks) {
     fa.n_qb = (a.N + kSparseQBlock - 1) / kSparseQBlock;
-    hipLaunchKernelGGL((anchor_fwd_kernel<kSparseQBlock / 32, kMinWaves, true>), dim3(fa.n_qb, heads),
+    hipLaunchKernelGGL((anchor_fwd_kernel<kSparseQBlock / 32, kMinWaves, true, false>), dim3(fa.n_qb, heads),
                        dim3(2 * kSparseQBlock), 0, stream, fa);
   } else {
     fa.n_qb = 0;
-    hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, false>),
+    hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, false, false>),
                        dim3((a.N + 32 * kWaves - 1) / (32 * kWaves), heads), dim3(64 * kWaves), 0, stream, fa);
   }
   return hipGetLastError();

@@ -126,6 +126,17 @@ struct AnchorArgs {
 size_t anchor_workspace_bytes(int B, int N, int H);
 hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream);
 
+struct AnchorBwdArgs {
+  int B, N, H;
+  const void *q, *k, *v, *g, *dO;
+  void *dq, *dk, *dv, *dg;
+  float scale;
+  void *ws;
+};
+
+size_t anchor_backward_workspace_bytes(int B, int N, int H);
+hipError_t launch_anchor_backward(const AnchorBwdArgs &a, hipStream_t stream);
+
 constexpr int kMaxSources = 16;
 
 struct RouteArgs {

@@ -38,6 +38,8 @@ EXPORTS = (
     "hla_softmax_anchor_workspace",
     "hla_softmax_anchor",
     "hla_softmax_anchor_block_sparse",
+    "hla_softmax_anchor_backward_workspace",
+    "hla_softmax_anchor_backward",
     "hla_attnres_route",
     "hla_status_string",
 )
@@ -109,6 +111,12 @@ def lib() -> ctypes.CDLL:
                                                       c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_int,
                                                       c_void_p, c_void_p, c_size_t, c_void_p]
         L.hla_softmax_anchor_block_sparse.restype = c_int
+        L.hla_softmax_anchor_backward_workspace.argtypes = [c_int, c_int, c_int, c_int]
+        L.hla_softmax_anchor_backward_workspace.restype = c_size_t
+        L.hla_softmax_anchor_backward.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                                  c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                  c_void_p, c_void_p, c_size_t, c_void_p]
+        L.hla_softmax_anchor_backward.restype = c_int
         L.hla_attnres_route.argtypes = [c_int, c_int, c_int, c_int, c_int, POINTER(c_void_p), c_void_p, c_void_p,
                                         c_float, c_void_p, c_void_p, c_void_p]
         L.hla_attnres_route.restype = c_int
@@ -341,6 +349,30 @@ def hla_softmax_anchor(q, k, v, g=None, scale: float | None = None, o=None, ws=N
                                   _ptr(o), _ptr(ws), nbytes, _stream(stream))
     _check(st, "hla_softmax_anchor")
     return o
+
+
+def hla_softmax_anchor_backward_workspace(B: int, N: int, H: int, D: int = 64) -> int:
+    return int(lib().hla_softmax_anchor_backward_workspace(B, N, H, D))
+
+
+def hla_softmax_anchor_backward(q, k, v, do, g=None, scale: float | None = None, dq=None, dk=None, dv=None, dg=None,
+                                ws=None, stream=None):
+    """Gradients of the gated softmax anchor (bf16); returns (dq, dk, dv, dg), dg None without g."""
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if g is not None and dg is None:
+        dg = torch.empty_like(g)
+    ws, nbytes = _workspace(hla_softmax_anchor_backward_workspace(B, N, H, D), q.device, ws)
+    st = lib().hla_softmax_anchor_backward(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                           float(scale), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                           _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_softmax_anchor_backward")
+    return dq, dk, dv, dg
 
 
 SPARSE_Q_BLOCK = 128  # query rows per block of the block-sparse anchor

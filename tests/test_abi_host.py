@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     assert sorted(hla.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -197,6 +197,28 @@ def test_anchor_validation(L):
     assert call(D=32) == E.HLA_ERR_UNSUPPORTED
     assert call(ws=None) == E.HLA_ERR_WORKSPACE
     assert call(ws_bytes=64 * 64 * 2 - 1) == E.HLA_ERR_WORKSPACE
+
+
+def test_anchor_backward_validation(L):
+    E = hla
+
+    def call(dt=0, N=8, D=64, scale=0.125, g=None, dg=None, dO=FAKE, dq=FAKE, ws_bytes=1 << 40):
+        return L.hla_softmax_anchor_backward(dt, 1, N, 1, D, FAKE, FAKE, FAKE, g, scale, dO, dq, FAKE, FAKE, dg,
+                                             FAKE, ws_bytes, None)
+
+    assert call(dO=None) == E.HLA_ERR_INVALID_ARG
+    assert call(dq=None) == E.HLA_ERR_INVALID_ARG
+    assert call(g=FAKE) == E.HLA_ERR_INVALID_ARG
+    assert call(dg=FAKE) == E.HLA_ERR_INVALID_ARG
+    assert call(scale=-1.0) == E.HLA_ERR_INVALID_ARG
+    assert call(N=0) == E.HLA_ERR_INVALID_ARG
+    assert call(dt=1) == E.HLA_ERR_UNSUPPORTED
+    assert call(D=32) == E.HLA_ERR_UNSUPPORTED
+    assert call(ws_bytes=1024) == E.HLA_ERR_WORKSPACE
+    # four transposed [64][Npad] copies, dY and two fp32 row vectors
+    n = hla.hla_softmax_anchor_backward_workspace(1, 75600, 32, 64)
+    assert n >= 4 * 32 * 64 * 75648 * 2 + 75600 * 32 * 64 * 2 + 2 * 75600 * 32 * 4
+    assert hla.hla_softmax_anchor_backward_workspace(1, 75600, 32, 48) == 0
 
 
 def test_sparse_anchor_validation(L):
