@@ -7,6 +7,7 @@ and independent library routines (torch's scaled_dot_product_attention).
 """
 import cmath
 import math
+import zlib
 
 import numpy as np
 import pytest
@@ -16,6 +17,14 @@ import oracle
 from oracle import Rope3D
 
 RNG = np.random.default_rng(1234)
+
+
+@pytest.fixture(autouse=True)
+def _seed_per_test(request):
+    """Each test draws from its own stream, seeded by its name, so its inputs do not depend on
+    which tests ran before it (test order varies with parallel workers)."""
+    global RNG
+    RNG = np.random.default_rng(zlib.crc32(request.node.name.encode()))
 
 
 # ----------------------------------------------------------------------------
