@@ -129,8 +129,8 @@ def main() -> int:
                          "counter reading calibrates bytes; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this library runs the path on one GPU; --gpus above 1 is not supported "
-                                   "(the multi-GPU sharding is described in DESIGN.md)"}), flush=True)
+        print(json.dumps({"error": "this library runs the path on one GPU; --gpus above 1 is not supported"}),
+              flush=True)
         return 2
 
     import numpy as np

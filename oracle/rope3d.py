@@ -6,7 +6,7 @@ ReLU feature map and then through a 3D RoPE; the pseudocode calls it
 ``apply_3d_rope(x, rope_freqs)`` without defining it. Section 4.1 says the
 head dimension was enlarged so that a 3D RoPE fits.
 
-Readings (the pages are silent on these; each is listed in the design doc):
+Readings (the pages are silent on these):
 
 * Token flattening: the notes flatten video tokens as T*H*W and reshape back
   as (B, T, H, W, ...) (section 3.3 pseudocode), so token n sits at
