@@ -275,12 +275,12 @@ hla_status hla_softmax_anchor_backward(hla_dtype dt, int B, int N, int H, int D,
  *   o_i = sigmoid(g_i) * sum_{j in K_r} softmax_{j in K_r}(scale q_i . k_j) v_j,
  * o_i = 0 when K_r is empty. blocks and counts are int32 DEVICE arrays. Counts
  * are clamped to [0, max_blocks]; entries outside [0, ceil(N / 64)) name
- * nothing and are skipped; named blocks must be distinct (a repeated entry is
- * visited twice, giving an unspecified result but no fault). Tiles are visited
- * in list order. Other arguments, workspace and numerics as hla_softmax_anchor
- * (same workspace size).
+ * nothing; the named blocks form a set (order and repeats do not matter; they
+ * are visited in ascending order). Other arguments, workspace and numerics as
+ * hla_softmax_anchor (same workspace size).
  * Errors: as hla_softmax_anchor, plus INVALID_ARG for null blocks/counts or
- * max_blocks <= 0.
+ * max_blocks <= 0, UNSUPPORTED for N above 1 677 312 (the key-block bitmaps
+ * must fit in 16 KB of LDS).
  */
 #define HLA_SPARSE_Q_BLOCK 128
 #define HLA_SPARSE_K_BLOCK 64

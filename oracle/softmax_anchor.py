@@ -70,8 +70,7 @@ def softmax_anchor_block_sparse(q, k, v, blocks, counts, g=None, scale: float | 
 
         o_i = sigmoid(g_i) * sum_{j in K_r} softmax_{j in K_r}(scale * q_i . k_j) v_j
 
-    and o_i = 0 when K_r is empty. Named blocks are taken as a set; the GPU
-    kernel expects them distinct.
+    and o_i = 0 when K_r is empty. Named blocks are taken as a set.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)

@@ -44,6 +44,10 @@ constexpr int kMinWaves = 4;       // waves per SIMD the forward kernel is compi
 static_assert(kSparseKBlock == kBK, "a named key block is one tile");
 static_assert(kSparseQBlock % 32 == 0, "a query block is whole waves of 32 rows");
 
+// bitmaps of the block-sparse form (dynamic LDS): the union of the work-group's
+// named tiles, then one set per query block of the work-group
+extern __shared__ __align__(16) uint32_t anchor_bits[];
+
 // Key position inside a group of 16 with bits 2 and 3 swapped. With this
 // order, the 8 keys a lane feeds to one 32x32x16 product (keys 4h..4h+3 and
 // 8+4h..8+4h+3 of a 16-key step, h = lane / 32) sit at positions 8h..8h+7.
@@ -118,9 +122,12 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // The row sum adds the bf16-rounded P with v_dot2 (two terms per
 // instruction): the normaliser uses the same weights as the P.V product.
-// kSparse: the work-group's query rows form one query block and visit only
-// the 64-key tiles named for it (entries outside the key range are skipped);
-// otherwise every tile in order. kPrep: the epilogue writes the inputs of the
+// kSparse: the work-group's query rows form WAVES / 4 query blocks of 128 rows.
+// The work-group walks the union of the 64-key tiles they name, in ascending
+// order (two LDS bitmaps: the union and each block's own set; entries outside
+// the key range name nothing, repeats count once), loading every tile once for
+// all its waves; a wave computes only the tiles its own block names.
+// Otherwise every tile in order. kPrep: the epilogue writes the inputs of the
 // gradient kernels instead of o (y = the ungated output, s = sigmoid(g)):
 // dG = dO y s (1 - s), dY = dO s (bf16), Delta = dY . y and L = mref + log2(rowsum),
 // so that p_ij = exp2(c s_ij - L_i) are the normalised weights.
@@ -191,31 +198,60 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
   float mref = -INFINITY, lsum = 0.f;
 
   const int ntiles = (a.N + kBK - 1) / kBK;
-  // position i of the visiting order -> key tile; next(i): first usable position >= i
-  const int *list = nullptr;
-  int cnt = ntiles;
+  constexpr int kBlockWaves = kSparseQBlock / 32;
+  const int nwords = (ntiles + 31) >> 5;
+  const uint32_t *uni = anchor_bits, *own = anchor_bits + (size_t)nwords * (1 + wave / kBlockWaves);
   if constexpr (kSparse) {
-    const size_t qblk = (size_t)bh * a.n_qb + blockIdx.x;
-    list = a.blocks + qblk * a.max_blocks;
-    cnt = min(max(a.counts[qblk], 0), a.max_blocks);
-  }
-  auto tile_of = [&](int i) { return kSparse ? list[i] : i; };
-  auto next = [&](int i) {
-    if constexpr (kSparse) {
-      while (i < cnt && (unsigned)list[i] >= (unsigned)ntiles) ++i;
+    for (int i = tid; i < nwords * (1 + WAVES / kBlockWaves); i += kThreads) anchor_bits[i] = 0u;
+    __syncthreads();
+    const int qb = blockIdx.x * (WAVES / kBlockWaves) + wave / kBlockWaves;
+    if (wave % kBlockWaves == 0 && qb < a.n_qb) {
+      const size_t qblk = (size_t)bh * a.n_qb + qb;
+      const int *list = a.blocks + qblk * a.max_blocks;
+      const int cnt = min(max(a.counts[qblk], 0), a.max_blocks);
+      uint32_t *mine = anchor_bits + (size_t)nwords * (1 + wave / kBlockWaves);
+      for (int i = lane; i < cnt; i += 64) {
+        const int m = list[i];
+        if ((unsigned)m < (unsigned)ntiles) {
+          atomicOr(&anchor_bits[m >> 5], 1u << (m & 31));
+          atomicOr(&mine[m >> 5], 1u << (m & 31));
+        }
+      }
     }
-    return i;
+    __syncthreads();
+  }
+  // first tile >= t in the visiting order, ntiles if none
+  auto next = [&](int t) {
+    if constexpr (!kSparse) {
+      return t;
+    } else {
+      int w = t >> 5;
+      if (w >= nwords) return ntiles;
+      uint32_t bits = uni[w] & (~0u << (t & 31));
+      while (bits == 0u) {
+        if (++w >= nwords) return ntiles;
+        bits = uni[w];
+      }
+      return (w << 5) + __builtin_ctz(bits);
+    }
   };
-  int pos = next(0);
-  if (pos < cnt) {
-    load_tile(tile_of(pos));
+  int t = next(0);
+  if (t < ntiles) {
+    load_tile(t);
     store_tile(0);
   }
   __syncthreads();
-  for (int buf = 0; pos < cnt; buf ^= 1) {
-    const int t = tile_of(pos);
-    const int pnext = next(pos + 1);
-    if (pnext < cnt) load_tile(tile_of(pnext));
+  for (int buf = 0; t < ntiles; buf ^= 1) {
+    const int tnext = next(t + 1);
+    if (tnext < ntiles) load_tile(tnext);
+    if (kSparse && !((own[t >> 5] >> (t & 31)) & 1u)) {  // not named by this wave's block
+      if (tnext < ntiles) {
+        store_tile(buf ^ 1);
+        __syncthreads();
+      }
+      t = tnext;
+      continue;
+    }
 
     // S^T = K Q^T for the 64 keys of this tile
     f32x16_t sacc[2];
@@ -305,11 +341,11 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
           oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kb][u], oacc[mb], 0, 0, 0);
         }
 
-    if (pnext < cnt) {
+    if (tnext < ntiles) {
       store_tile(buf ^ 1);  // the other buffer was last read two tiles ago
       __syncthreads();
     }
-    pos = pnext;
+    t = tnext;
   }
 
   // normalise, gate, store: lane holds row tl, dims 32*mb + 8*i + 4*half + j
@@ -760,6 +796,11 @@ hipError_t launch_anchor_backward(const AnchorBwdArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+size_t anchor_sparse_lds_bytes(int N) {
+  const size_t nwords = (((size_t)N + kBK - 1) / kBK + 31) / 32;
+  return nwords * (1 + kWaves / (kSparseQBlock / 32)) * sizeof(uint32_t);
+}
+
 size_t anchor_workspace_bytes(int B, int N, int H) {
   const size_t npad = ((size_t)N + kBK - 1) / kBK * kBK;
   return (size_t)B * H * kD * npad * sizeof(uint16_t);
@@ -786,8 +827,9 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   fa.max_blocks = a.max_blocks;
   if (a.blocks) {
     fa.n_qb = (a.N + kSparseQBlock - 1) / kSparseQBlock;
-    hipLaunchKernelGGL((anchor_fwd_kernel<kSparseQBlock / 32, kMinWaves, true, false>), dim3(fa.n_qb, heads),
-                       dim3(2 * kSparseQBlock), 0, stream, fa);
+    hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, true, false>),
+                       dim3((a.N + 32 * kWaves - 1) / (32 * kWaves), heads), dim3(64 * kWaves),
+                       anchor_sparse_lds_bytes(a.N), stream, fa);
   } else {
     fa.n_qb = 0;
     hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, false, false>),

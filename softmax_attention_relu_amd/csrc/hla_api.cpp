@@ -303,7 +303,7 @@ hla_status hla_softmax_anchor_block_sparse(hla_dtype dt, int B, int N, int H, in
                                            hipStream_t stream) {
   if (!q || !k || !v || !o || !blocks || !counts) return HLA_ERR_INVALID_ARG;
   if (!shape_ok(B, N, H) || !isfinite(scale) || !(scale > 0.f) || max_blocks <= 0) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
+  if (dt != HLA_BF16 || D != kD || anchor_sparse_lds_bytes(N) > kSparseLdsLimit) return HLA_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < anchor_workspace_bytes(B, N, H)) return HLA_ERR_WORKSPACE;
   AnchorArgs a;
   a.B = B;

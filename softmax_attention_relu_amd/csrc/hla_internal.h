@@ -124,6 +124,8 @@ struct AnchorArgs {
 };
 
 size_t anchor_workspace_bytes(int B, int N, int H);
+size_t anchor_sparse_lds_bytes(int N);      // bitmaps of the block-sparse form
+constexpr size_t kSparseLdsLimit = 16384;  // larger N is rejected (N above ~1.6M tokens)
 hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream);
 
 struct AnchorBwdArgs {

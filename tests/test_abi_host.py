@@ -236,6 +236,7 @@ def test_sparse_anchor_validation(L):
     assert call(dt=1) == E.HLA_ERR_UNSUPPORTED
     assert call(D=32) == E.HLA_ERR_UNSUPPORTED
     assert call(ws_bytes=64 * 64 * 2 - 1) == E.HLA_ERR_WORKSPACE
+    assert call(N=1677312 + 64 * 32) == E.HLA_ERR_UNSUPPORTED  # key-block bitmaps above 16 KB of LDS
     src = open(os.path.join(ROOT, "include", "hla.h")).read()
     assert "#define HLA_SPARSE_Q_BLOCK 128" in src and hla.SPARSE_Q_BLOCK == 128
     assert "#define HLA_SPARSE_K_BLOCK 64" in src and hla.SPARSE_K_BLOCK == 64

@@ -3,9 +3,10 @@
 The oracle is ``oracle.softmax_anchor_block_sparse`` (pinned in
 tests/test_oracle.py; parity against the pages is unpinned, as they give no
 pattern). Cases: random patterns with empty lists, entries that name nothing,
-counts beyond max_blocks and negative counts, ragged query and key blocks; the
-full pattern in natural order, which must equal the dense kernel bit for bit;
-and the 720p/5s local-window pattern on sampled rows.
+repeated entries, counts beyond max_blocks and negative counts, ragged query
+and key blocks, and work-groups whose four query blocks name different tiles;
+every key block named, which must equal the dense kernel bit for bit; and the
+720p/5s local-window pattern on sampled rows.
 """
 import numpy as np
 import pytest
@@ -31,6 +32,8 @@ def random_pattern(rng, B, H, N, max_blocks):
                 named = rng.permutation(nkb)[:c]
                 if c and rng.random() < 0.3:
                     named[0] = nkb + int(rng.integers(0, 5))  # names nothing
+                if c > 2 and rng.random() < 0.3:
+                    named[-1] = named[1]  # a repeat counts once
                 blocks[b, h, r, :len(named)] = named
                 counts[b, h, r] = len(named)
     # a count beyond max_blocks (clamped) and a negative count (none)
@@ -70,11 +73,12 @@ def test_sparse_anchor_random_patterns(N, B, H, gated):
 
 
 def test_sparse_anchor_full_pattern_equals_dense():
-    """Every key block named in order: each wave walks the dense kernel's tiles, so the outputs match bitwise."""
+    """Every key block named (in reverse order): each wave walks the dense kernel's tiles in ascending order, so
+    the outputs match bitwise."""
     B, N, H = 1, 1000, 5
     x = {nm: synth.randn(930, (B, N, H, 64), stream=i) for i, nm in enumerate("qkvg")}
     nqb, nkb = -(-N // 128), -(-N // 64)
-    blocks = np.tile(np.arange(nkb, dtype=np.int32), (B, H, nqb, 1))
+    blocks = np.tile(np.arange(nkb, dtype=np.int32)[::-1].copy(), (B, H, nqb, 1))
     counts = np.full((B, H, nqb), nkb, dtype=np.int32)
     o = run(x, blocks, counts)
     d = {k: dev(v) for k, v in x.items()}
