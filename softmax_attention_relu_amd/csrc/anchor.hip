@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void anchor_vt_kernel(VtArgs a) {
     const int key = c >> 3, dc = c & 7;
     const int n = n0 + key;
     uint4 w = make_uint4(0, 0, 0, 0);
-    if (n < a.N) w = *reinterpret_cast<const uint4 *>(vp + (size_t)n * tok_stride + 8 * dc);
+    if (n < a.N) w = load_once_u4(vp + (size_t)n * tok_stride + 8 * dc);
     uint32_t *dst = reinterpret_cast<uint32_t *>(&tile[key][8 * dc]);
     dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
   }

@@ -94,6 +94,22 @@ __device__ __forceinline__ void store_nt(uint16_t *p, u32x4_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
 }
 
+// Loads of data a kernel reads exactly once, where each load instruction
+// covers whole 128-byte lines (eight lanes x 16 bytes of a bf16 token row):
+// non-temporal, so the stream does not displace the lines work-groups share
+// (states, RoPE tables, the anchor's key tiles). Streams that use them ran
+// 5-11% faster. Where several instructions read pieces of one line (8-byte
+// loads, fp32 rows split over two loads) ordinary loads keep the line for the
+// later pieces; a non-temporal load there fetched it again (the token-causal
+// kernel slowed from 0.74 to 1.2 ms).
+__device__ __forceinline__ u32x4_t load_once16(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+__device__ __forceinline__ uint4 load_once_u4(const void *p) {
+  const u32x4_t v = load_once16(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Orders this wave's LDS stores before its later LDS loads (and the reverse)
 // without a work-group barrier: LDS requests of one wave are served in order,
 // the fence keeps the compiler from moving them across.

@@ -42,7 +42,7 @@ struct Elem<true> {
   };
   __device__ static Chunk load(const T *p) {
     Chunk c;
-    c.w = *reinterpret_cast<const uint4 *>(p);
+    c.w = load_once_u4(p);
     return c;
   }
   __device__ static Chunk zero() {
@@ -602,8 +602,8 @@ __global__ __launch_bounds__(256, kRopeMode == kRopePair ? 1 : 2) void la_apply_
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const size_t n = (size_t)min(sub + 8 * u + r8, hi - 1);
-      qrow[u] = *reinterpret_cast<const u32x4_t *>(qp + n * tok_stride);
-      if constexpr (kGate) grow[u] = *reinterpret_cast<const u32x4_t *>(gp + n * tok_stride);
+      qrow[u] = load_once16(qp + n * tok_stride);
+      if constexpr (kGate) grow[u] = load_once16(gp + n * tok_stride);
     }
     f32x2_t cs[kRope ? 4 : 1][4];
     if constexpr (kRope) {

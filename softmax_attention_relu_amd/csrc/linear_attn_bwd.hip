@@ -121,7 +121,7 @@ __device__ __forceinline__ void load_rows(const uint16_t *p, size_t stride, int 
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const size_t n = (size_t)min(sub + 8 * u + r8, hi - 1);
-    rows[u] = *reinterpret_cast<const u32x4_t *>(p + n * stride);
+    rows[u] = load_once16(p + n * stride);
   }
 }
 

@@ -25,7 +25,7 @@ struct RouteElem<true> {
   };
   __device__ static Chunk load(const void *base, size_t off) {
     Chunk c;
-    c.w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + off);
+    c.w = load_once_u4(reinterpret_cast<const uint16_t *>(base) + off);
     return c;
   }
   __device__ static void unpack(const Chunk &c, float x[8]) {
@@ -35,8 +35,8 @@ struct RouteElem<true> {
     x[6] = bf16_lo(c.w.w); x[7] = bf16_hi(c.w.w);
   }
   __device__ static void store(void *base, size_t off, const float y[8]) {
-    *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(base) + off) =
-        make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7]));
+    store_nt(reinterpret_cast<uint16_t *>(base) + off,
+             u32x4_t{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])});
   }
 };
 template <>
@@ -56,9 +56,9 @@ struct RouteElem<false> {
     x[4] = c.b.x; x[5] = c.b.y; x[6] = c.b.z; x[7] = c.b.w;
   }
   __device__ static void store(void *base, size_t off, const float y[8]) {
-    float *p = reinterpret_cast<float *>(base) + off;
-    *reinterpret_cast<float4 *>(p) = make_float4(y[0], y[1], y[2], y[3]);
-    *reinterpret_cast<float4 *>(p + 4) = make_float4(y[4], y[5], y[6], y[7]);
+    f32x4_t *p = reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(base) + off);
+    __builtin_nontemporal_store(f32x4_t{y[0], y[1], y[2], y[3]}, p);
+    __builtin_nontemporal_store(f32x4_t{y[4], y[5], y[6], y[7]}, p + 1);
   }
 };
 
