@@ -591,8 +591,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void anchor_dkdv_kernel(BwdArgs a) {
 }
 
 template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 2) void anchor_dq_kernel(BwdArgs a) {
-  static_assert(64 * WAVES == kBK * 8, "one 16-byte chunk of each tile per thread");
+__global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
+  constexpr int kLoaders = kBK * 8;  // threads that stage one 16-byte chunk of each tile
   __shared__ __align__(16) uint16_t ks[2][kBK * kKRow];   // K rows of the key tile
   __shared__ __align__(16) uint16_t vr[2][kBK * kKRow];   // V rows
   __shared__ __align__(16) uint16_t kts[2][kD * kVRow];  // K^T, permuted
@@ -617,6 +617,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void anchor_dq_kernel(BwdArgs a) {
   const int row = tid >> 3, ch = tid & 7;
   uint4 sreg[3];
   auto load_tile = [&](int t) {
+    if (tid >= kLoaders) return;
     const int n0 = t * kBK, n = n0 + row;
     const uint4 z = make_uint4(0, 0, 0, 0);
     sreg[0] = n < a.N ? *reinterpret_cast<const uint4 *>(kp + (size_t)n * tok_stride + 8 * ch) : z;
@@ -624,6 +625,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void anchor_dq_kernel(BwdArgs a) {
     sreg[2] = *reinterpret_cast<const uint4 *>(ktp + (size_t)row * a.npad + n0 + 8 * ch);
   };
   auto store_tile = [&](int buf) {
+    if (tid >= kLoaders) return;
     *reinterpret_cast<uint4 *>(&ks[buf][row * kKRow + 8 * ch]) = sreg[0];
     *reinterpret_cast<uint4 *>(&vr[buf][row * kKRow + 8 * ch]) = sreg[1];
     *reinterpret_cast<uint4 *>(&kts[buf][row * kVRow + 8 * ch]) = sreg[2];
@@ -642,52 +644,45 @@ __global__ __launch_bounds__(64 * WAVES, 2) void anchor_dq_kernel(BwdArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1);
-    // S^T and dP^T of the tile's 64 keys (rows) against the wave's 32 queries
-    f32x16_t sacc[2], pacc[2];
+    const bool tail = (t + 1) * kBK > a.N;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // S^T and dP^T of 32 of the tile's keys (rows) against the wave's 32 queries
+      f32x16_t sacc, pacc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = pacc[kb][i] = 0.f;
+      for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int off = (32 * kb + tl) * kKRow + 16 * s + 8 * half;
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&ks[buf][off]), qb[s],
-                                                           sacc[kb], 0, 0, 0);
-        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&vr[buf][off]), db[s],
-                                                           pacc[kb], 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&ks[buf][off]), qb[s], sacc,
+                                                       0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&vr[buf][off]), db[s], pacc,
+                                                       0, 0, 0);
       }
-    }
-    const bool tail = (t + 1) * kBK > a.N;
-    bf16x8_t sw[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
       float dv[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * i + j;
-          float pj = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], a.c, -L));
+          float pj = __builtin_amdgcn_exp2f(fmaf(sacc[e], a.c, -L));
           if (tail && t * kBK + 32 * kb + 8 * i + 4 * half + j >= a.N) pj = 0.f;
-          dv[e] = pj * (pacc[kb][e] - Dl);
+          dv[e] = pj * (pacc[e] - Dl);
         }
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        sw[kb][u] = __builtin_bit_cast(
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8_t sw = __builtin_bit_cast(
             bf16x8_t, make_uint4(pack_bf16(dv[8 * u], dv[8 * u + 1]), pack_bf16(dv[8 * u + 2], dv[8 * u + 3]),
                                  pack_bf16(dv[8 * u + 4], dv[8 * u + 5]), pack_bf16(dv[8 * u + 6], dv[8 * u + 7])));
-    }
-    // dQ^T += K^T dS^T over the tile's keys
+        // dQ^T += K^T dS^T over these keys
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int mb = 0; mb < 2; ++mb) {
           const int off = (32 * mb + tl) * kVRow + 32 * kb + 16 * u + 8 * half;
-          dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&kts[buf][off]),
-                                                            sw[kb][u], dqa[mb], 0, 0, 0);
+          dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&kts[buf][off]), sw,
+                                                            dqa[mb], 0, 0, 0);
         }
+      }
+    }
     if (t + 1 < ntiles) {
       store_tile(buf ^ 1);
       __syncthreads();
@@ -792,7 +787,11 @@ hipError_t launch_anchor_backward(const AnchorBwdArgs &a, hipStream_t stream) {
   const dim3 grid((a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves), heads);
   hipLaunchKernelGGL((anchor_dkdv_kernel<kBwdWaves>), grid, dim3(64 * kBwdWaves), 0, stream, ba);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((anchor_dq_kernel<kBwdWaves>), grid, dim3(64 * kBwdWaves), 0, stream, ba);
+  // dq: the tile's two 32-key blocks one after the other keep it within 128
+  // registers, so it runs sixteen waves (four per SIMD) like the forward
+  constexpr int kDqWaves = 16;
+  hipLaunchKernelGGL((anchor_dq_kernel<kDqWaves>), dim3((a.N + 32 * kDqWaves - 1) / (32 * kDqWaves), heads),
+                     dim3(64 * kDqWaves), 0, stream, ba);
   return hipGetLastError();
 }
 
