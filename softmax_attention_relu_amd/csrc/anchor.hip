@@ -253,16 +253,18 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
       continue;
     }
 
-    // S^T = K Q^T for the 64 keys of this tile
+    // S^T = K Q^T for the 64 keys of this tile; here and in the P.V product the
+    // two accumulators alternate, so each product waits on the other's
+    // predecessor rather than its own
     f32x16_t sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int kb = 0; kb < 2; ++kb) {
         const bf16x8_t kv =
             *reinterpret_cast<const bf16x8_t *>(&ks[buf][(32 * kb + tl) * kKRow + 16 * s + 8 * half]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qb[s], sacc[kb], 0, 0, 0);
@@ -331,11 +333,11 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int mb = 0; mb < 2; ++mb) {
           const bf16x8_t vv =
               *reinterpret_cast<const bf16x8_t *>(&vs[buf][(32 * mb + tl) * kVRow + 32 * kb + 16 * u + 8 * half]);
           oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kb][u], oacc[mb], 0, 0, 0);
@@ -436,6 +438,16 @@ struct BwdArgs {
   float c, scale;
 };
 
+// 16 bytes at p, or zeros when ok is false (p is then not read). Written as a
+// branch on purpose: a select between the loaded value and a named zero vector
+// can be turned into a load through a selected pointer, which puts the zero
+// vector (and the staged tile) in scratch memory.
+__device__ __forceinline__ uint4 chunk_or_zero(const uint16_t *p, bool ok) {
+  uint4 w = make_uint4(0, 0, 0, 0);
+  if (ok) w = *reinterpret_cast<const uint4 *>(p);
+  return w;
+}
+
 // B operands of 32 tokens' rows: lane (tl, half) holds token n (its wave's
 // token tl), dims 16 s + 8 half .. +7 (zero past N)
 __device__ __forceinline__ void row_operands(const uint16_t *base, size_t stride, int n, int half, int N,
@@ -492,15 +504,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void anchor_dkdv_kernel(BwdArgs a) {
   float sf = 0.f;
   auto load_tile = [&](int t) {
     const int n0 = t * kBK, n = n0 + row;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    sreg[0] = n < a.N ? *reinterpret_cast<const uint4 *>(qp + (size_t)n * tok_stride + 8 * ch) : z;
-    sreg[1] = n < a.N ? *reinterpret_cast<const uint4 *>(dp + (size_t)n * tok_stride + 8 * ch) : z;
+    sreg[0] = chunk_or_zero(qp + (size_t)n * tok_stride + 8 * ch, n < a.N);
+    sreg[1] = chunk_or_zero(dp + (size_t)n * tok_stride + 8 * ch, n < a.N);
     sreg[2] = *reinterpret_cast<const uint4 *>(qtp + (size_t)row * a.npad + n0 + 8 * ch);
     sreg[3] = *reinterpret_cast<const uint4 *>(dtp + (size_t)row * a.npad + n0 + 8 * ch);
-    if (tid < 2 * kBK) {
-      const int qn = n0 + (tid & (kBK - 1));
-      // past N: a weight of exactly 0 and no Delta
-      sf = tid < kBK ? (qn < a.N ? lsp[qn] : INFINITY) : (qn < a.N ? dlp[qn] : 0.f);
+    // past N: a weight of exactly 0 and no Delta (waves 0 and 1 read L and Delta)
+    const int qn = n0 + (tid & (kBK - 1));
+    if (tid < kBK) {
+      sf = INFINITY;
+      if (qn < a.N) sf = lsp[qn];
+    } else if (tid < 2 * kBK) {
+      sf = 0.f;
+      if (qn < a.N) sf = dlp[qn];
     }
   };
   auto store_tile = [&](int buf) {
@@ -590,12 +605,21 @@ __global__ __launch_bounds__(64 * WAVES, 2) void anchor_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// Tiles of the dq kernel go global -> LDS directly (no staging registers):
+// rows of 128 bytes, unpadded, with row r's 16-byte chunk c in slot c ^ (r & 7),
+// so the 8 rows that one operand read touches per chunk column fall in 8
+// different slots. One copy instruction moves 8 rows (64 lanes x 16 bytes).
+__device__ __forceinline__ void copy_rows(const uint16_t *src, uint16_t *lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
-  constexpr int kLoaders = kBK * 8;  // threads that stage one 16-byte chunk of each tile
-  __shared__ __align__(16) uint16_t ks[2][kBK * kKRow];   // K rows of the key tile
-  __shared__ __align__(16) uint16_t vr[2][kBK * kKRow];   // V rows
-  __shared__ __align__(16) uint16_t kts[2][kD * kVRow];  // K^T, permuted
+  static_assert(WAVES == 16, "waves 0-7 copy K and V rows, waves 8-15 copy K^T rows");
+  __shared__ __align__(16) uint16_t ks[2][kBK * kD];   // K rows of the key tile
+  __shared__ __align__(16) uint16_t vr[2][kBK * kD];   // V rows
+  __shared__ __align__(16) uint16_t kts[2][kD * kBK];  // K^T, permuted
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -614,22 +638,25 @@ __global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
   const uint16_t *kp = a.k + head_base, *vp = a.v + head_base;
   const uint16_t *ktp = a.kt + (size_t)bh * kD * a.npad;
 
-  const int row = tid >> 3, ch = tid & 7;
-  uint4 sreg[3];
-  auto load_tile = [&](int t) {
-    if (tid >= kLoaders) return;
-    const int n0 = t * kBK, n = n0 + row;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    sreg[0] = n < a.N ? *reinterpret_cast<const uint4 *>(kp + (size_t)n * tok_stride + 8 * ch) : z;
-    sreg[1] = n < a.N ? *reinterpret_cast<const uint4 *>(vp + (size_t)n * tok_stride + 8 * ch) : z;
-    sreg[2] = *reinterpret_cast<const uint4 *>(ktp + (size_t)row * a.npad + n0 + 8 * ch);
+  // copier: wave w copies rows 8 (w % 8) .. +7; lane i takes row + i / 8 and
+  // fills slot i % 8 with chunk (i % 8) ^ (row & 7)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int crow = 8 * (wv & 7) + (lane >> 3);
+  const int cchunk = (lane & 7) ^ (crow & 7);
+  auto issue_tile = [&](int t, int buf) {
+    const int n0 = t * kBK;
+    if (wv < 8) {
+      const int n = min(n0 + crow, a.N - 1);  // rows past the end: finite data, weight 0
+      copy_rows(kp + (size_t)n * tok_stride + 8 * cchunk, &ks[buf][512 * wv]);
+      copy_rows(vp + (size_t)n * tok_stride + 8 * cchunk, &vr[buf][512 * wv]);
+    } else {
+      copy_rows(ktp + (size_t)crow * a.npad + n0 + 8 * cchunk, &kts[buf][512 * (wv - 8)]);
+    }
   };
-  auto store_tile = [&](int buf) {
-    if (tid >= kLoaders) return;
-    *reinterpret_cast<uint4 *>(&ks[buf][row * kKRow + 8 * ch]) = sreg[0];
-    *reinterpret_cast<uint4 *>(&vr[buf][row * kKRow + 8 * ch]) = sreg[1];
-    *reinterpret_cast<uint4 *>(&kts[buf][row * kVRow + 8 * ch]) = sreg[2];
-  };
+  // this lane's operand rows tl (+ 32 per block): chunk 2j + half sits in slot (2j + half) ^ (tl & 7)
+  int roff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) roff[j] = tl * kD + 8 * ((2 * j + half) ^ (tl & 7));
 
   f32x16_t dqa[2];
 #pragma unroll
@@ -638,12 +665,13 @@ __global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
     for (int i = 0; i < 16; ++i) dqa[mb][i] = 0.f;
 
   const int ntiles = (a.N + kBK - 1) / kBK;
-  load_tile(0);
-  store_tile(0);
+  issue_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+    // the other buffers held tile t - 1, whose readers all passed the last barrier
+    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
     const bool tail = (t + 1) * kBK > a.N;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -653,7 +681,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
       for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int off = (32 * kb + tl) * kKRow + 16 * s + 8 * half;
+        const int off = 32 * kb * kD + roff[s];
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&ks[buf][off]), qb[s], sacc,
                                                        0, 0, 0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&vr[buf][off]), db[s], pacc,
@@ -677,14 +705,14 @@ __global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
         // dQ^T += K^T dS^T over these keys
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const int off = (32 * mb + tl) * kVRow + 32 * kb + 16 * u + 8 * half;
+          const int off = 32 * mb * kBK + roff[2 * kb + u];
           dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&kts[buf][off]), sw,
                                                             dqa[mb], 0, 0, 0);
         }
       }
     }
     if (t + 1 < ntiles) {
-      store_tile(buf ^ 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t + 1 has landed
       __syncthreads();
     }
   }
