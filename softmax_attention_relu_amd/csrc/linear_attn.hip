@@ -829,6 +829,7 @@ struct CausalArgs {
   float eps;
   const float *prefix;  // inclusive prefix per range: [B*H][n_chunks][kStateFloats]
   const float *init;    // state before the first range: [B*H][kStateFloats]
+  int tab_t, tab_h, tab_w;  // floats in each band's table (LDS-staged RoPE)
 };
 
 __device__ __forceinline__ int key_perm(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
@@ -859,8 +860,24 @@ __device__ __forceinline__ f32x4_t rope_run(const RopeArgs &r, const TokenPos &t
   return *reinterpret_cast<const f32x4_t *>(col + (size_t)pos * stride);
 }
 
-template <bool kRope, bool kGate>
+// the same from the LDS copy of the tables, laid out [t table | h table | w table]
+__device__ __forceinline__ f32x4_t rope_run_lds(const RopeArgs &r, const CausalArgs &a, const TokenPos &tp, int d) {
+  int i;
+  if (d < r.d_t)
+    i = d + (int)tp.t * r.d_t;
+  else if (d < r.d_t + r.d_h)
+    i = a.tab_t + (d - r.d_t) + (int)tp.y * r.d_h;
+  else
+    i = a.tab_t + a.tab_h + (d - r.d_t - r.d_h) + (int)tp.x * r.d_w;
+  return *reinterpret_cast<const f32x4_t *>(&la_tab_lds[i]);
+}
+
+// kRopeMode: kRopeNone, kRopeGlobal (tables read from global memory) or
+// kRopeLds (tables copied to LDS first: every lookup of a step would otherwise
+// be a global round trip on the step's critical path)
+template <int kRopeMode, bool kGate>
 __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
+  constexpr bool kRope = kRopeMode != kRopeNone;
   __shared__ __align__(16) uint16_t ct_all[kHeadsPerWG][kD * kCtRow];
   __shared__ __align__(16) uint16_t vt_all[kHeadsPerWG][kD * kCtRow];
   __shared__ __align__(16) float z_all[kHeadsPerWG][kD];
@@ -870,8 +887,20 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
   const int half = lane >> 5, tl = lane & 31;
   const int hgroup = blockIdx.x % a.ngroups;
   const int rng = blockIdx.x / a.ngroups;
+  if constexpr (kRopeMode == kRopeLds) {
+    // copy the three tables into LDS (each a multiple of 4 floats)
+    const int n4 = (a.tab_t + a.tab_h + a.tab_w) / 4;
+    for (int i = tid; i < n4; i += 256) {
+      const int f = 4 * i;
+      const float *src = f < a.tab_t ? a.rope.cs_t + f
+                                      : (f < a.tab_t + a.tab_h ? a.rope.cs_h + (f - a.tab_t)
+                                                               : a.rope.cs_w + (f - a.tab_t - a.tab_h));
+      *reinterpret_cast<f32x4_t *>(&la_tab_lds[f]) = *reinterpret_cast<const f32x4_t *>(src);
+    }
+    __syncthreads();
+  }
   const int h = kHeadsPerWG * hgroup + wave;
-  if (h >= a.H) return;  // no work-group barrier in this kernel
+  if (h >= a.H) return;  // no work-group barrier follows
   const int b = blockIdx.y;
   const int bh = b * a.H + h;
   const int lo = rng * a.L;
@@ -1003,7 +1032,11 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
       if constexpr (kRope) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const f32x4_t c4 = rope_run(a.rope, tp, d0 + 8 * u);
+          f32x4_t c4;
+          if constexpr (kRopeMode == kRopeLds)
+            c4 = rope_run_lds(a.rope, a, tp, d0 + 8 * u);
+          else
+            c4 = rope_run(a.rope, tp, d0 + 8 * u);
           rotate(qa[4 * u], qa[4 * u + 1], f32x2_t{c4.x, c4.y});
           rotate(qa[4 * u + 2], qa[4 * u + 3], f32x2_t{c4.z, c4.w});
           rotate(kc[4 * u], kc[4 * u + 1], f32x2_t{c4.x, c4.y});
@@ -1094,9 +1127,18 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
           sacc[kb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cta[kb], vtb[nb], sacc[kb][nb], 0, 0, 0);
     }
 
-    // normalise, gate, store: lane holds dims 32*mb + 8i + 4*half + j of token n
+    // normalise, gate, store: lane holds dims 32*mb + 8i + 4*half + j of token n.
+    // The gate pieces are all loaded before the first store (a store to o
+    // could otherwise be taken to alias the next gate load, one round trip each).
     const float inv = 1.f / den;
     if (valid) {
+      uint2 gws[2][4];
+      if constexpr (kGate) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gws[mb][i] = *reinterpret_cast<const uint2 *>(a.g + row + 32 * mb + 8 * i + 4 * half);
+      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -1106,7 +1148,7 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) y[j] = oacc[mb][4 * i + j] * inv;
           if constexpr (kGate) {
-            const uint2 gw = *reinterpret_cast<const uint2 *>(a.g + off);
+            const uint2 gw = gws[mb][i];
             y[0] *= sigmoid_fast(bf16_lo(gw.x));
             y[1] *= sigmoid_fast(bf16_hi(gw.x));
             y[2] *= sigmoid_fast(bf16_lo(gw.y));
@@ -1310,6 +1352,15 @@ LinearPlan plan_linear_causal(int B, int N, int H) {
   return p;
 }
 
+template <int kRopeMode>
+void launch_causal(bool gate, dim3 grid, const CausalArgs &ca, hipStream_t stream) {
+  const size_t lds = kRopeMode == kRopeLds ? (size_t)(ca.tab_t + ca.tab_h + ca.tab_w) * sizeof(float) : 0;
+  if (gate)
+    hipLaunchKernelGGL((la_causal_kernel<kRopeMode, true>), grid, dim3(256), lds, stream, ca);
+  else
+    hipLaunchKernelGGL((la_causal_kernel<kRopeMode, false>), grid, dim3(256), lds, stream, ca);
+}
+
 hipError_t launch_linear_causal(const LinearArgs &a, const LinearPlan &p, hipStream_t stream) {
   float *prefix = nullptr;
   float *init = reinterpret_cast<float *>(reinterpret_cast<char *>(a.ws) + p.init_offset);
@@ -1332,19 +1383,21 @@ hipError_t launch_linear_causal(const LinearArgs &a, const LinearPlan &p, hipStr
   ca.eps = a.eps;
   ca.prefix = prefix;
   ca.init = init;
+  ca.tab_t = ca.tab_h = ca.tab_w = 0;
+  if (a.rope.enabled) {
+    ca.tab_t = (int)((uint32_t)a.N / a.rope.hw) * a.rope.d_t;
+    ca.tab_h = (int)a.rope.h * a.rope.d_h;
+    ca.tab_w = (int)a.rope.w * a.rope.d_w;
+  }
+  const int tab_floats = ca.tab_t + ca.tab_h + ca.tab_w;
   const dim3 grid(p.n_chunks * p.ngroups, a.B);
   const bool gate = a.g != nullptr;
-  if (a.rope.enabled) {
-    if (gate)
-      hipLaunchKernelGGL((la_causal_kernel<true, true>), grid, dim3(256), 0, stream, ca);
-    else
-      hipLaunchKernelGGL((la_causal_kernel<true, false>), grid, dim3(256), 0, stream, ca);
-  } else {
-    if (gate)
-      hipLaunchKernelGGL((la_causal_kernel<false, true>), grid, dim3(256), 0, stream, ca);
-    else
-      hipLaunchKernelGGL((la_causal_kernel<false, false>), grid, dim3(256), 0, stream, ca);
-  }
+  if (!a.rope.enabled)
+    launch_causal<kRopeNone>(gate, grid, ca, stream);
+  else if (tab_floats <= kTabLdsFloats)
+    launch_causal<kRopeLds>(gate, grid, ca, stream);
+  else
+    launch_causal<kRopeGlobal>(gate, grid, ca, stream);
   return hipGetLastError();
 }
 
