@@ -68,6 +68,27 @@ def test_causal_small_shapes(N, rope, gated, carry):
     assert normwise(host(kso), ks_ref) <= 1e-5
 
 
+@pytest.mark.parametrize("grid", [(600, 1, 1), (1, 2, 300), (8, 12, 10)])
+def test_causal_rope_table_paths(grid):
+    """RoPE table sets of up to 9 216 floats (36 KB) are read from an LDS copy (8x12x10: 656
+    floats; 1x2x300: 7 264, a long w table), larger ones from global memory (600x1x1: 9 648).
+    Each against the oracle, gated, with a carried state."""
+    B, H = 1, 2
+    N = grid[0] * grid[1] * grid[2]
+    x = {nm: synth.randn(760 + N, (B, N, H, 64), stream=i) for i, nm in enumerate("qkvg")}
+    kv_in = synth.randn(761, (B, H, 64, 64), dtype="f32").astype(np.float64)
+    ks_in = np.abs(synth.randn(762, (B, H, 64), dtype="f32").astype(np.float64)) * 10
+    floats = grid[0] * 16 + grid[1] * 24 + grid[2] * 24
+    say(f"[causal] rope grid {grid}: {floats} table floats ({'global' if floats > 9216 else 'LDS'} lookups)")
+    o, kvo, kso = run_causal(x, grid, kv_in, ks_in)
+    ref, kv_ref, ks_ref = oracle_causal(x, grid, kv_in, ks_in)
+    e = normwise(host(o), ref)
+    say(f"[causal] rope grid {grid}: normwise {e:.3e}")
+    assert e <= TOL_BF16
+    assert normwise(host(kvo), kv_ref) <= TOL_BF16
+    assert normwise(host(kso), ks_ref) <= 1e-5
+
+
 def test_causal_in_place_state_determinism_and_resume():
     """kv_out == kv_in updates in place; two calls carrying the state equal one call; repeats are bitwise equal."""
     grid = (10, 10, 10)
