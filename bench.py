@@ -46,10 +46,13 @@ def _dev(torch, x):
 
 
 def _src_hash(*names) -> str:
+    """Hash of the kernel sources and of the build script (its flags shape the code too)."""
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "softmax_attention_relu_amd", "csrc", n), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(ROOT, "softmax_attention_relu_amd", "build.py"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 

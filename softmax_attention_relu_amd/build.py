@@ -30,9 +30,20 @@ FLAGS = [
 ]
 
 
+# Per-source device flags. The anchor kernels take row maxima of matrix-core
+# results with fmaxf; in the GPU's IEEE mode every such max first quiets
+# signalling NaNs (one extra instruction per operand the compiler cannot prove
+# canonical). Their inputs carry no NaN semantics (masked scores are -inf), so
+# the anchor's device code runs with IEEE mode off. Host code keeps full NaN
+# handling (the API's argument checks rely on it).
+DEVICE_FLAGS = {
+    "anchor.hip": ["-Xarch_device", "-mno-amdgpu-ieee", "-Xarch_device", "-fno-honor-nans"],
+}
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *DEVICE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
