@@ -931,6 +931,15 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
   const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD;
   const int kp_self = key_perm(tl);
 
+  // v rows of the next step are loaded one step ahead (right after this step's
+  // V^T is in LDS), so a step does not start by waiting for them
+  uint4 vnext[4];
+  {
+    const int hi0 = min(hi_r, lo + kApplySub);
+    const size_t row0 = head_base + (size_t)min(lo + tl, hi0 - 1) * tok_stride;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) vnext[s] = *reinterpret_cast<const uint4 *>(a.v + row0 + 16 * s + 8 * half);
+  }
   for (int sub = lo; sub < hi_r; sub += kApplySub) {
     const int hi = min(hi_r, sub + kApplySub);
     const int n = sub + tl;
@@ -941,7 +950,7 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
     // state's dim order (8-byte pieces)
     uint4 vp[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) vp[s] = *reinterpret_cast<const uint4 *>(a.v + row + 16 * s + 8 * half);
+    for (int s = 0; s < 4; ++s) vp[s] = vnext[s];
     TokenPos tp;
     if constexpr (kRope) tp = token_pos(a.rope, (uint32_t)min(n, hi - 1));
     if (!valid) {
@@ -956,6 +965,14 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
         vt[(16 * s + 8 * half + t) * kCtRow + kp_self] = (uint16_t)((t & 1) ? (w[t >> 1] >> 16) : (w[t >> 1] & 0xFFFFu));
+    }
+
+    if (sub + kApplySub < hi_r) {
+      const int nn = sub + kApplySub + tl;
+      const int hin = min(hi_r, sub + 2 * kApplySub);
+      const size_t rown = head_base + (size_t)min(nn, hin - 1) * tok_stride;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) vnext[s] = *reinterpret_cast<const uint4 *>(a.v + rown + 16 * s + 8 * half);
     }
 
     f32x16_t tacc, uacc, oacc[2];
