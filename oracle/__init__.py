@@ -28,6 +28,8 @@ pages' order of operations:
                      abstract and summary, hybrid 3:1 design).
 * ``softmax_anchor_backward`` -- gradients of the gated anchor, derived by
                      hand from its definition.
+* ``softmax_anchor_lse`` -- the natural-log normaliser of every query row
+                     (what a backward pass reuses instead of the forward).
 * ``softmax_anchor_block_sparse`` -- the anchor restricted to caller-given
                      key blocks per query block (the pages name a sparse
                      anchor without its pattern: parity unpinned against them).
@@ -43,7 +45,7 @@ RoPE pairing and frequency convention (the pages do not define
 from .rope3d import Rope3D, rope3d_angles, rope3d_rotate
 from .linear_attention import (linear_attention, linear_attention_backward, linear_attention_causal,
                                linear_attention_chunked, linear_attention_chunked_backward)
-from .softmax_anchor import softmax_anchor, softmax_anchor_backward, softmax_anchor_block_sparse
+from .softmax_anchor import softmax_anchor, softmax_anchor_backward, softmax_anchor_block_sparse, softmax_anchor_lse
 from .attnres_router import attnres_route
 
 __all__ = [
@@ -58,5 +60,6 @@ __all__ = [
     "softmax_anchor",
     "softmax_anchor_block_sparse",
     "softmax_anchor_backward",
+    "softmax_anchor_lse",
     "attnres_route",
 ]

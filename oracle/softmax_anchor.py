@@ -56,6 +56,30 @@ def softmax_anchor(q, k, v, g=None, scale: float | None = None, rows=None, row_b
     return out
 
 
+def softmax_anchor_lse(q, k, scale: float | None = None, rows=None, row_block: int = 256):
+    """Natural-log normaliser of every query row, lse_i = log sum_j exp(scale q_i . k_j), fp64.
+
+    Returned as (B, H, len(rows)). With it the weights are p_ij = exp(l_ij - lse_i),
+    which is what a backward pass reuses instead of recomputing the forward.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, N, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    out = np.empty((B, H, len(rows)))
+    for b in range(B):
+        for h in range(H):
+            kh = k[b, :, h, :]
+            for r0 in range(0, len(rows), row_block):
+                rr = rows[r0:r0 + row_block]
+                logits = scale * (q[b, rr, h, :] @ kh.T)
+                m = logits.max(axis=1)
+                out[b, h, r0:r0 + len(rr)] = m + np.log(np.exp(logits - m[:, None]).sum(axis=1))
+    return out
+
+
 def softmax_anchor_block_sparse(q, k, v, blocks, counts, g=None, scale: float | None = None, q_block: int = 128,
                                 k_block: int = 64, rows=None):
     """Block-sparse gated softmax anchor, fp64 (parity unpinned against the pages).

@@ -680,6 +680,32 @@ def test_sparse_anchor_one_block_and_empty():
     assert np.all(got[:, 128:] == 0)
 
 
+def test_anchor_lse_pins():
+    """softmax_anchor_lse: zero keys give log N exactly, one key gives scale q.k, and in general it
+    equals scipy's logsumexp of the logits; exp(l - lse) rows sum to one and, applied to V,
+    reproduce softmax_anchor."""
+    from scipy.special import logsumexp
+
+    rng = np.random.default_rng(5)
+    B, N, H, D = 2, 37, 3, 16
+    q = rng.standard_normal((B, N, H, D)) * 3
+    k = rng.standard_normal((B, N, H, D))
+    v = rng.standard_normal((B, N, H, D))
+    lse = oracle.softmax_anchor_lse(q, np.zeros_like(k), scale=0.25)
+    assert np.allclose(lse, np.log(N), rtol=0, atol=1e-14)
+    lse1 = oracle.softmax_anchor_lse(q[:, :1], k[:, :1], scale=0.25)
+    assert np.allclose(lse1[:, :, 0], 0.25 * np.einsum("bhd,bhd->bh", q[:, 0], k[:, 0]), rtol=0, atol=1e-12)
+    lse = oracle.softmax_anchor_lse(q, k, scale=0.25, rows=[0, 5, 36])
+    for b in range(B):
+        for h in range(H):
+            logits = 0.25 * q[b, [0, 5, 36], h] @ k[b, :, h].T
+            assert np.allclose(lse[b, h], logsumexp(logits, axis=1), rtol=1e-13, atol=0)
+            p = np.exp(logits - lse[b, h][:, None])
+            assert np.allclose(p.sum(axis=1), 1.0, atol=1e-13)
+            ref = oracle.softmax_anchor(q, k, v, None, 0.25, rows=[0, 5, 36])[b, :, h]
+            assert np.allclose(p @ v[b, :, h], ref, atol=1e-12)
+
+
 def test_anchor_special_cases():
     B, N, H, D = 1, 16, 1, 64
     q, v = _randn(B, N, H, D), _randn(B, N, H, D)
