@@ -394,7 +394,33 @@ def main() -> int:
             "mfma_frac": ab_alg / (ab_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "schedule_tflops": ab_sched / (ab_ms * 1e-3) / 1e12}
         log(f"[bench] anchor backward 720p/5s: {ab_ms:.1f} ms")
-        del ado, aws, agrads
+        # the same gradients from a saved forward (its gated output and row normalisers): the
+        # second forward pass becomes an elementwise preparation, 14 N^2 D scheduled
+        ao, alse = hla.hla_softmax_anchor_lse(anc["q"], anc["k"], anc["v"], anc["g"], aw.scale)
+
+        def abwd_saved_call():
+            hla.hla_softmax_anchor_backward_saved(anc["q"], anc["k"], anc["v"], ao, alse, ado, anc["g"], aw.scale,
+                                                  *agrads, ws=aws)
+
+        abwd_saved_call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(2):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            abwd_saved_call()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        as_ms = float(np.mean(times))
+        as_sched = 14.0 * aw.B * aw.H * float(aw.N) ** 2 * aw.D
+        out["legs"]["anchor_backward_saved_720p5s"] = {
+            "N": aw.N, "ms": as_ms, "algorithmic_flop": ab_alg, "schedule_flop": as_sched,
+            "algorithmic_tflops": ab_alg / (as_ms * 1e-3) / 1e12,
+            "mfma_frac": ab_alg / (as_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "schedule_tflops": as_sched / (as_ms * 1e-3) / 1e12}
+        log(f"[bench] anchor backward from the saved forward 720p/5s: {as_ms:.1f} ms")
+        del ado, aws, agrads, ao, alse
 
     # ---------------- block-sparse anchor leg: 720p/5s with a local-window pattern
     if not args.no_legs:

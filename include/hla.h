@@ -15,11 +15,13 @@
  *                            gradients of the bidirectional and block-causal
  *                            variants (inputs, gate and carried state).
  *   hla_softmax_anchor       gated non-causal softmax attention (the periodic
- *                            full-rank anchor layer).
+ *                            full-rank anchor layer); hla_softmax_anchor_lse
+ *                            also writes each row's normaliser.
  *   hla_softmax_anchor_block_sparse
  *                            the anchor restricted to caller-given key blocks.
- *   hla_softmax_anchor_backward
- *                            gradients of the anchor.
+ *   hla_softmax_anchor_backward, hla_softmax_anchor_backward_saved
+ *                            gradients of the anchor, recomputing the forward
+ *                            or from its saved output and normalisers.
  *   hla_attnres_route        block attention-residual (AttnRes) depth router.
  *
  * Conventions shared by every entry point
@@ -240,6 +242,21 @@ hla_status hla_softmax_anchor(hla_dtype dt, int B, int N, int H, int D,
                               float scale, void *o, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * hla_softmax_anchor that also writes each row's normaliser (the log-sum-exp
+ * that FlashAttention-style training keeps for the backward pass):
+ *   lse[(b*H + h)*N + n] = log sum_j exp(scale * q_n . k_j)   (natural log)
+ * for batch b, head h, query n. lse: device float [B][H][N], caller-owned. It is
+ * the log of the forward's own normaliser (the sum of its bf16-rounded weights
+ * relative to its running max), so exp(scale q.k - lse) are exactly the weights
+ * the forward used, up to float rounding. Same workspace as hla_softmax_anchor.
+ * Errors: as hla_softmax_anchor, plus INVALID_ARG for a null lse.
+ */
+hla_status hla_softmax_anchor_lse(hla_dtype dt, int B, int N, int H, int D,
+                                  const void *q, const void *k, const void *v, const void *g,
+                                  float scale, void *o, float *lse, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/*
  * Gradients of hla_softmax_anchor (bf16). Given the forward's inputs and dO, the
  * gradient of a scalar loss with respect to o, it writes dq, dk, dv and dg (the
  * latter when g is given). With p_ij the softmax weights, y_i = sum_j p_ij v_j
@@ -262,6 +279,24 @@ hla_status hla_softmax_anchor_backward(hla_dtype dt, int B, int N, int H, int D,
                                        float scale, const void *dO,
                                        void *dq, void *dk, void *dv, void *dg,
                                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hla_softmax_anchor_backward from a saved forward: o and lse as written by
+ * hla_softmax_anchor_lse for the same q, k, v, g and scale. The second forward
+ * pass is replaced by an elementwise preparation, with s = sigmoid(g):
+ *   dY = dO s,  dg = dO o (1 - s),  Delta = dO . o   (= dY . y),
+ * and the weights are p_ij = exp(scale q_i . k_j - lse_i). The results match
+ * hla_softmax_anchor_backward up to rounding (Delta is formed from o instead of
+ * the bf16 dY and the float y, and dg from the bf16 o). o: [B][N][H][D] bf16,
+ * lse: float [B][H][N]; the other arguments and the workspace as
+ * hla_softmax_anchor_backward. Repeated calls are bitwise identical.
+ * Errors: as hla_softmax_anchor_backward, plus INVALID_ARG for a null o or lse.
+ */
+hla_status hla_softmax_anchor_backward_saved(hla_dtype dt, int B, int N, int H, int D,
+                                             const void *q, const void *k, const void *v, const void *g,
+                                             float scale, const void *o, const float *lse, const void *dO,
+                                             void *dq, void *dk, void *dv, void *dg,
+                                             void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Block-sparse form of hla_softmax_anchor. The pages name a sparse anchor

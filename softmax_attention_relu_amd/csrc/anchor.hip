@@ -116,6 +116,8 @@ struct FwdArgs {
   const uint16_t *dO;
   uint16_t *dg, *dy;
   float *lse, *delta;  // [B*H][N]
+  // optional (not kPrep): the natural-log normaliser of every row, [B*H][N]
+  float *lse_out;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -398,6 +400,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     return;
   }
   if (n < a.N) {
+    if (a.lse_out && half == 0) a.lse_out[(size_t)bh * a.N + n] = (mref + log2f(l)) * 0.6931471805599453f;
     const size_t row = head_base + (size_t)n * tok_stride;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -720,6 +723,64 @@ __global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
   if (n < a.N) store_cols(a.dq + head_base, tok_stride, n, half, dqa, a.scale);
 }
 
+// Preparation from a saved forward: with o the gated output (o = s y, s = sigmoid(g))
+// and lse its natural-log row normaliser, per row and dim
+//   dY = dO s (bf16), dG = dO o (1 - s), Delta = sum_d dO o, L = lse log2(e).
+// Delta is dO . o = dY . y in exact arithmetic (the recomputing preparation uses the
+// bf16 dY instead, which it has next to y). Eight threads per (token, head) row,
+// eight dims each.
+struct PrepArgs {
+  const uint16_t *o, *g, *dO;
+  const float *lse;  // natural log, [B*H][N]
+  uint16_t *dy, *dg;
+  float *L, *delta;  // log2 units, [B*H][N]
+  long long rows;    // B * N * H
+  int N, H;
+};
+
+__global__ __launch_bounds__(256) void anchor_prep_saved_kernel(PrepArgs a) {
+  const long long r = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int part = threadIdx.x & 7;
+  const long long rr = r < a.rows ? r : a.rows - 1;  // the row's 8 threads stay together
+  const size_t off = (size_t)rr * kD + 8 * part;
+  const uint4 ow = *reinterpret_cast<const uint4 *>(a.o + off);
+  const uint4 dw = *reinterpret_cast<const uint4 *>(a.dO + off);
+  uint4 gw = make_uint4(0, 0, 0, 0);
+  if (a.g) gw = *reinterpret_cast<const uint4 *>(a.g + off);
+  const uint32_t ov[4] = {ow.x, ow.y, ow.z, ow.w}, dv[4] = {dw.x, dw.y, dw.z, dw.w}, gv[4] = {gw.x, gw.y, gw.z, gw.w};
+  uint32_t dyw[4], dgw[4];
+  float part_delta = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float dy2[2], dg2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float o = e ? bf16_hi(ov[w]) : bf16_lo(ov[w]);
+      const float d = e ? bf16_hi(dv[w]) : bf16_lo(dv[w]);
+      const float s = a.g ? __builtin_amdgcn_rcpf(1.f + __expf(-(e ? bf16_hi(gv[w]) : bf16_lo(gv[w])))) : 1.f;
+      dy2[e] = d * s;
+      dg2[e] = d * o * (1.f - s);
+      part_delta += d * o;
+    }
+    dyw[w] = pack_bf16(dy2[0], dy2[1]);
+    dgw[w] = pack_bf16(dg2[0], dg2[1]);
+  }
+  part_delta += __shfl_xor(part_delta, 1);
+  part_delta += __shfl_xor(part_delta, 2);
+  part_delta += __shfl_xor(part_delta, 4);
+  if (r >= a.rows) return;
+  *reinterpret_cast<uint4 *>(a.dy + off) = make_uint4(dyw[0], dyw[1], dyw[2], dyw[3]);
+  if (a.g) *reinterpret_cast<uint4 *>(a.dg + off) = make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]);
+  if (part == 0) {
+    const int h = (int)(r % a.H);
+    const long long bn = r / a.H;
+    const int n = (int)(bn % a.N), b = (int)(bn / a.N);
+    const size_t i = ((size_t)b * a.H + h) * a.N + n;
+    a.L[i] = a.lse[i] * 1.4426950408889634f;
+    a.delta[i] = part_delta;
+  }
+}
+
 hipError_t launch_vt(const void *x, void *xt, int B, int N, int H, int npad, hipStream_t stream) {
   VtArgs va;
   va.v = reinterpret_cast<const uint16_t *>(x);
@@ -767,28 +828,45 @@ hipError_t launch_anchor_backward(const AnchorBwdArgs &a, hipStream_t stream) {
   uint16_t *dy = reinterpret_cast<uint16_t *>(ws + l.dy);
   float *lse = reinterpret_cast<float *>(ws + l.lse), *delta = reinterpret_cast<float *>(ws + l.delta);
 
-  hipError_t e = launch_vt(a.v, vt, a.B, a.N, a.H, npad, stream);
-  if (e != hipSuccess) return e;
-  // preparation: the forward with its epilogue writing dG, dY, L, Delta
+  hipError_t e;
   FwdArgs fa;
   memset(&fa, 0, sizeof(fa));
-  fa.q = reinterpret_cast<const uint16_t *>(a.q);
-  fa.k = reinterpret_cast<const uint16_t *>(a.k);
-  fa.g = reinterpret_cast<const uint16_t *>(a.g);
-  fa.vt = vt;
-  fa.N = a.N;
-  fa.H = a.H;
-  fa.npad = npad;
   fa.c = a.scale * 1.4426950408889634f;
-  fa.dO = reinterpret_cast<const uint16_t *>(a.dO);
-  fa.dg = reinterpret_cast<uint16_t *>(a.dg);
-  fa.dy = dy;
-  fa.lse = lse;
-  fa.delta = delta;
-  hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, false, true>),
-                     dim3((a.N + 32 * kWaves - 1) / (32 * kWaves), heads), dim3(64 * kWaves), 0, stream, fa);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (a.o && a.lse) {
+    // preparation from the saved forward: elementwise, no second forward pass
+    PrepArgs pa;
+    pa.o = reinterpret_cast<const uint16_t *>(a.o);
+    pa.g = reinterpret_cast<const uint16_t *>(a.g);
+    pa.dO = reinterpret_cast<const uint16_t *>(a.dO);
+    pa.lse = a.lse;
+    pa.dy = dy;
+    pa.dg = reinterpret_cast<uint16_t *>(a.dg);
+    pa.L = lse;
+    pa.delta = delta;
+    pa.rows = (long long)a.B * a.N * a.H;
+    pa.N = a.N;
+    pa.H = a.H;
+    hipLaunchKernelGGL(anchor_prep_saved_kernel, dim3((unsigned)((pa.rows + 31) / 32)), dim3(256), 0, stream, pa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    if ((e = launch_vt(a.v, vt, a.B, a.N, a.H, npad, stream)) != hipSuccess) return e;
+    // preparation: the forward with its epilogue writing dG, dY, L, Delta
+    fa.q = reinterpret_cast<const uint16_t *>(a.q);
+    fa.k = reinterpret_cast<const uint16_t *>(a.k);
+    fa.g = reinterpret_cast<const uint16_t *>(a.g);
+    fa.vt = vt;
+    fa.N = a.N;
+    fa.H = a.H;
+    fa.npad = npad;
+    fa.dO = reinterpret_cast<const uint16_t *>(a.dO);
+    fa.dg = reinterpret_cast<uint16_t *>(a.dg);
+    fa.dy = dy;
+    fa.lse = lse;
+    fa.delta = delta;
+    hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, false, true>),
+                       dim3((a.N + 32 * kWaves - 1) / (32 * kWaves), heads), dim3(64 * kWaves), 0, stream, fa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if ((e = launch_vt(a.q, qt, a.B, a.N, a.H, npad, stream)) != hipSuccess) return e;
   if ((e = launch_vt(dy, dyt, a.B, a.N, a.H, npad, stream)) != hipSuccess) return e;
   if ((e = launch_vt(a.k, kt, a.B, a.N, a.H, npad, stream)) != hipSuccess) return e;
@@ -840,6 +918,7 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   if (e != hipSuccess) return e;
 
   FwdArgs fa;
+  memset(&fa, 0, sizeof(fa));
   fa.q = reinterpret_cast<const uint16_t *>(a.q);
   fa.k = reinterpret_cast<const uint16_t *>(a.k);
   fa.g = reinterpret_cast<const uint16_t *>(a.g);
@@ -852,6 +931,7 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   fa.blocks = a.blocks;
   fa.counts = a.counts;
   fa.max_blocks = a.max_blocks;
+  fa.lse_out = a.lse;
   if (a.blocks) {
     fa.n_qb = (a.N + kSparseQBlock - 1) / kSparseQBlock;
     hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, true, false>),

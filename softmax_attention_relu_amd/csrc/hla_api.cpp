@@ -265,6 +265,29 @@ hla_status hla_softmax_anchor(hla_dtype dt, int B, int N, int H, int D, const vo
   return launch_anchor(a, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
 }
 
+hla_status hla_softmax_anchor_lse(hla_dtype dt, int B, int N, int H, int D, const void *q, const void *k,
+                                  const void *v, const void *g, float scale, void *o, float *lse, void *ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  if (!lse) return HLA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o) return HLA_ERR_INVALID_ARG;
+  if (!shape_ok(B, N, H) || !isfinite(scale) || !(scale > 0.f)) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < anchor_workspace_bytes(B, N, H)) return HLA_ERR_WORKSPACE;
+  AnchorArgs a;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.o = o;
+  a.scale = scale;
+  a.ws = ws;
+  a.lse = lse;
+  return launch_anchor(a, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
+}
+
 size_t hla_softmax_anchor_backward_workspace(int B, int N, int H, int D) {
   if (!shape_ok(B, N, H) || D != kD) return 0;
   return anchor_backward_workspace_bytes(B, N, H);
@@ -294,6 +317,36 @@ hla_status hla_softmax_anchor_backward(hla_dtype dt, int B, int N, int H, int D,
   a.dg = dg;
   a.scale = scale;
   a.ws = ws;
+  return launch_anchor_backward(a, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
+}
+
+hla_status hla_softmax_anchor_backward_saved(hla_dtype dt, int B, int N, int H, int D, const void *q, const void *k,
+                                             const void *v, const void *g, float scale, const void *o,
+                                             const float *lse, const void *dO, void *dq, void *dk, void *dv, void *dg,
+                                             void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!o || !lse) return HLA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !dO || !dq || !dk || !dv) return HLA_ERR_INVALID_ARG;
+  if ((g == nullptr) != (dg == nullptr)) return HLA_ERR_INVALID_ARG;
+  if (!shape_ok(B, N, H) || !isfinite(scale) || !(scale > 0.f)) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < anchor_backward_workspace_bytes(B, N, H)) return HLA_ERR_WORKSPACE;
+  AnchorBwdArgs a;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.dO = dO;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = dg;
+  a.scale = scale;
+  a.ws = ws;
+  a.o = o;
+  a.lse = lse;
   return launch_anchor_backward(a, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
 }
 

@@ -121,6 +121,7 @@ struct AnchorArgs {
   void *ws;
   const int *blocks = nullptr, *counts = nullptr;  // block-sparse form when blocks != nullptr
   int max_blocks = 0;
+  float *lse = nullptr;  // optional: natural-log normaliser per row, [B*H][N]
 };
 
 size_t anchor_workspace_bytes(int B, int N, int H);
@@ -134,6 +135,10 @@ struct AnchorBwdArgs {
   void *dq, *dk, *dv, *dg;
   float scale;
   void *ws;
+  // saved forward (both or neither): its gated output and row normalisers; then
+  // the preparation is elementwise instead of a second forward pass
+  const void *o = nullptr;
+  const float *lse = nullptr;
 };
 
 size_t anchor_backward_workspace_bytes(int B, int N, int H);

@@ -37,9 +37,11 @@ EXPORTS = (
     "hla_linear_attn_chunked_backward",
     "hla_softmax_anchor_workspace",
     "hla_softmax_anchor",
+    "hla_softmax_anchor_lse",
     "hla_softmax_anchor_block_sparse",
     "hla_softmax_anchor_backward_workspace",
     "hla_softmax_anchor_backward",
+    "hla_softmax_anchor_backward_saved",
     "hla_attnres_route",
     "hla_status_string",
 )
@@ -107,6 +109,9 @@ def lib() -> ctypes.CDLL:
         L.hla_softmax_anchor.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_float, c_void_p, c_void_p, c_size_t, c_void_p]
         L.hla_softmax_anchor.restype = c_int
+        L.hla_softmax_anchor_lse.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.hla_softmax_anchor_lse.restype = c_int
         L.hla_softmax_anchor_block_sparse.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
                                                       c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_int,
                                                       c_void_p, c_void_p, c_size_t, c_void_p]
@@ -117,6 +122,11 @@ def lib() -> ctypes.CDLL:
                                                   c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
                                                   c_void_p, c_void_p, c_size_t, c_void_p]
         L.hla_softmax_anchor_backward.restype = c_int
+        L.hla_softmax_anchor_backward_saved.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                                                        c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p,
+                                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                                        c_void_p]
+        L.hla_softmax_anchor_backward_saved.restype = c_int
         L.hla_attnres_route.argtypes = [c_int, c_int, c_int, c_int, c_int, POINTER(c_void_p), c_void_p, c_void_p,
                                         c_float, c_void_p, c_void_p, c_void_p]
         L.hla_attnres_route.restype = c_int
@@ -351,6 +361,24 @@ def hla_softmax_anchor(q, k, v, g=None, scale: float | None = None, o=None, ws=N
     return o
 
 
+def hla_softmax_anchor_lse(q, k, v, g=None, scale: float | None = None, o=None, lse=None, ws=None, stream=None):
+    """Gated softmax anchor (bf16) that also writes each row's natural-log normaliser; returns (o, lse),
+    lse float [B, H, N]."""
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws, nbytes = _workspace(hla_softmax_anchor_workspace(B, N, H, D), q.device, ws)
+    st = lib().hla_softmax_anchor_lse(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
+                                      _ptr(o), _ptr(lse), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_softmax_anchor_lse")
+    return o, lse
+
+
 def hla_softmax_anchor_backward_workspace(B: int, N: int, H: int, D: int = 64) -> int:
     return int(lib().hla_softmax_anchor_backward_workspace(B, N, H, D))
 
@@ -372,6 +400,29 @@ def hla_softmax_anchor_backward(q, k, v, do, g=None, scale: float | None = None,
                                            float(scale), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
                                            _ptr(ws), nbytes, _stream(stream))
     _check(st, "hla_softmax_anchor_backward")
+    return dq, dk, dv, dg
+
+
+def hla_softmax_anchor_backward_saved(q, k, v, o, lse, do, g=None, scale: float | None = None, dq=None, dk=None,
+                                      dv=None, dg=None, ws=None, stream=None):
+    """Gradients of the gated softmax anchor from its saved output o and normalisers lse (as written by
+    hla_softmax_anchor_lse); returns (dq, dk, dv, dg), dg None without g."""
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 of shape (B, H, N)")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if g is not None and dg is None:
+        dg = torch.empty_like(g)
+    ws, nbytes = _workspace(hla_softmax_anchor_backward_workspace(B, N, H, D), q.device, ws)
+    st = lib().hla_softmax_anchor_backward_saved(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                                 float(scale), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                                 _ptr(dv), _ptr(dg), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_softmax_anchor_backward_saved")
     return dq, dk, dv, dg
 
 

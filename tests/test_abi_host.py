@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     assert sorted(hla.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -219,6 +219,32 @@ def test_anchor_backward_validation(L):
     n = hla.hla_softmax_anchor_backward_workspace(1, 75600, 32, 64)
     assert n >= 4 * 32 * 64 * 75648 * 2 + 75600 * 32 * 64 * 2 + 2 * 75600 * 32 * 4
     assert hla.hla_softmax_anchor_backward_workspace(1, 75600, 32, 48) == 0
+
+
+def test_anchor_saved_forward_validation(L):
+    """The forward that writes row normalisers and the backward from a saved forward reject a missing
+    lse or o, then check the rest as their base calls do (no GPU work is reached)."""
+    E = hla
+
+    def fwd(lse=FAKE, q=FAKE, dt=0, D=64, ws_bytes=1 << 40):
+        return L.hla_softmax_anchor_lse(dt, 1, 8, 1, D, q, FAKE, FAKE, None, 0.125, FAKE, lse, FAKE, ws_bytes, None)
+
+    assert fwd(lse=None) == E.HLA_ERR_INVALID_ARG
+    assert fwd(q=None) == E.HLA_ERR_INVALID_ARG
+    assert fwd(dt=1) == E.HLA_ERR_UNSUPPORTED
+    assert fwd(D=32) == E.HLA_ERR_UNSUPPORTED
+    assert fwd(ws_bytes=16) == E.HLA_ERR_WORKSPACE
+
+    def bwd(o=FAKE, lse=FAKE, g=None, dg=None, dO=FAKE, N=8, ws_bytes=1 << 40):
+        return L.hla_softmax_anchor_backward_saved(0, 1, N, 1, 64, FAKE, FAKE, FAKE, g, 0.125, o, lse, dO, FAKE, FAKE,
+                                                   FAKE, dg, FAKE, ws_bytes, None)
+
+    assert bwd(o=None) == E.HLA_ERR_INVALID_ARG
+    assert bwd(lse=None) == E.HLA_ERR_INVALID_ARG
+    assert bwd(dO=None) == E.HLA_ERR_INVALID_ARG
+    assert bwd(g=FAKE) == E.HLA_ERR_INVALID_ARG
+    assert bwd(N=0) == E.HLA_ERR_INVALID_ARG
+    assert bwd(ws_bytes=1024) == E.HLA_ERR_WORKSPACE
 
 
 def test_sparse_anchor_validation(L):

@@ -104,3 +104,68 @@ def test_anchor_backward_720p5s():
         r_k = np.abs(dkh.sum(axis=1)).max() / np.abs(dkh).sum(axis=1).max()
         say(f"[anchor bwd] head {h}: dq {e_q:.3e} dg {e_g:.3e} sum dv {e_v:.3e} |sum dk|/sum|dk| {r_k:.2e}")
         assert e_q <= TOL_BF16 and e_g <= TOL_BF16 and e_v <= TOL_BF16 and r_k <= 1e-3
+
+
+@pytest.mark.parametrize("N", [1, 65, 300, 1000])
+@pytest.mark.parametrize("gated", [True, False])
+def test_anchor_lse_and_saved_backward(N, gated):
+    """hla_softmax_anchor_lse: o bitwise equal to hla_softmax_anchor, lse against the oracle's
+    normaliser (max abs 1e-2: a relative error of 1e-2 in the weights); the backward from that
+    saved o and lse against the oracle gradients."""
+    B, H = 2, 3
+    x = inputs(1100 + N, B, N, H, gated)
+    d = {k: dev(v) for k, v in x.items()}
+    o, lse = hla.hla_softmax_anchor_lse(d["q"], d["k"], d["v"], d.get("g"), 0.125)
+    o_plain = hla.hla_softmax_anchor(d["q"], d["k"], d["v"], d.get("g"), 0.125)
+    grads = hla.hla_softmax_anchor_backward_saved(d["q"], d["k"], d["v"], o, lse, d["do"], d.get("g"), 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain)
+    f = {k: synth.to_f64(v) for k, v in x.items()}
+    lse_ref = oracle.softmax_anchor_lse(f["q"], f["k"], 0.125)
+    e_lse = np.abs(host(lse) - lse_ref).max()
+    say(f"[anchor saved] N={N} gated={gated}: lse max abs {e_lse:.3e}")
+    assert e_lse <= 1e-2
+    ref = oracle.softmax_anchor_backward(f["q"], f["k"], f["v"], f["do"], f.get("g"), 0.125)
+    names = ("dq", "dk", "dv", "dg") if gated else ("dq", "dk", "dv")
+    for nm, got, r in zip(names, grads, ref):
+        if N == 1 and nm in ("dq", "dk"):
+            # one key: dq, dk vanish; bound them by the size of the cancelling terms
+            s = 1.0 if not gated else 1.0 / (1.0 + np.exp(-f["g"]))
+            term = np.abs(np.sum(f["do"] * s * f["v"], axis=-1, keepdims=True))
+            other = f["k"] if nm == "dq" else f["q"]
+            assert np.abs(host(got)).max() <= TOL_BF16 * 0.125 * np.max(term * np.abs(other)), nm
+            continue
+        e = normwise(host(got), r)
+        say(f"[anchor saved] N={N} {nm}: {e:.3e}")
+        assert e <= TOL_BF16, nm
+    if not gated:
+        assert grads[3] is None
+
+
+def test_anchor_saved_backward_720p5s():
+    """720p/5s (B1 H32 N75600, gated): the backward from the saved forward against the recomputing
+    backward (normwise) and through the identities sum_j dv_j = sum_i dY_i and sum_j dk_j = 0."""
+    w = synth.HYBRID_ANCHOR
+    x = w.draw()
+    x["do"] = synth.randn(w.seed, (w.B, w.N, w.H, w.D), stream=4)
+    d = {k: dev(v) for k, v in x.items()}
+    say(f"[anchor saved] {w.name}: N={w.N} H={w.H}")
+    o, lse = hla.hla_softmax_anchor_lse(d["q"], d["k"], d["v"], d["g"], w.scale)
+    saved = hla.hla_softmax_anchor_backward_saved(d["q"], d["k"], d["v"], o, lse, d["do"], d["g"], w.scale)
+    again = hla.hla_softmax_anchor_backward_saved(d["q"], d["k"], d["v"], o, lse, d["do"], d["g"], w.scale)
+    full = hla.hla_softmax_anchor_backward(d["q"], d["k"], d["v"], d["do"], d["g"], w.scale)
+    torch.cuda.synchronize()
+    for a, b in zip(saved, again):
+        assert torch.equal(a, b)
+    for nm, a, b in zip(("dq", "dk", "dv", "dg"), saved, full):
+        e = normwise(host(a), host(b).astype(np.float64))
+        say(f"[anchor saved] {nm} vs recomputing backward: {e:.3e}")
+        assert e <= TOL_BF16, nm
+    for h in (0, 31):
+        f = {k: synth.to_f64(v[:, :, h:h + 1]) for k, v in x.items()}
+        dy_sum = np.sum(f["do"] / (1.0 + np.exp(-f["g"])), axis=1)
+        e_v = normwise(host(saved[2][:, :, h:h + 1].float().sum(dim=1)), dy_sum)
+        dkh = host(saved[1][:, :, h:h + 1])
+        r_k = np.abs(dkh.sum(axis=1)).max() / np.abs(dkh).sum(axis=1).max()
+        say(f"[anchor saved] head {h}: sum dv {e_v:.3e} |sum dk|/sum|dk| {r_k:.2e}")
+        assert e_v <= TOL_BF16 and r_k <= 1e-3
