@@ -4,7 +4,9 @@
 //   alpha = softmax_i(l),                 h = sum_i alpha_i v_i
 // RMSNorm reduces to the scalar r_i, so each source is read from HBM once:
 // a wave handles one token at a time, every lane holding 8-element chunks of
-// each source in registers (chunk c of the row lives in lane c % 64). The two
+// each source in registers (chunk c of the row lives in lane c % 64); u, the
+// same for every token of a batch, sits in a per-wave LDS copy, which keeps
+// the kernel within 128 registers and four waves per SIMD for C <= 2048. The two
 // dot products of all sources are summed over the wave in one transposed
 // butterfly, then the weighted sum is formed from the registers. Sources that
 // do not fit in registers are read again for the weighted sum.
@@ -132,40 +134,43 @@ __device__ __forceinline__ void wave_sums(float v[VC], float red[VC]) {
 // window of the sources. CHL: 8-element chunks per lane (C <= 512 * CHL).
 // kKeep: sources kept in registers (S <= kKeep), otherwise the weighted sum
 // reads the row again. SMAX: sources the reduction is sized for (S <= SMAX).
+extern __shared__ __align__(16) float route_u_lds[];
+
 template <bool kBF16, int CHL, int kKeep, int SMAX>
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+__global__ __launch_bounds__(256, CHL <= 4 ? 4 : 1) void route_kernel(RouteArgs a) {
   typedef RouteElem<kBF16> E;
   const int lane = threadIdx.x & 63;
+  // u = w + phi_t[b] of the wave's current batch, one copy per wave in LDS
+  float *ul = route_u_lds + (size_t)(threadIdx.x >> 6) * a.C;
   const long long tokens = (long long)a.B * a.T;
   const long long nwaves = (long long)gridDim.x * 4;
   const int nch = a.C / 8;
   const float inv_c = 1.f / (float)a.C;
 
-  float u[CHL][8];
-  int ub = -1;  // batch whose u is loaded
+  int ub = -1;  // batch whose u is staged
   for (long long tok = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); tok < tokens; tok += nwaves) {
     const int b = (int)(tok / a.T);
     if (b != ub) {  // u = w + phi_t[b]
       ub = b;
+      wave_lds_fence();  // the previous batch's u is no longer read
 #pragma unroll
       for (int c = 0; c < CHL; ++c) {
         const int ch = lane + 64 * c;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) u[c][t] = 0.f;
         if (ch < nch) {
-          const float4 w0 = *reinterpret_cast<const float4 *>(a.w + 8 * ch);
-          const float4 w1 = *reinterpret_cast<const float4 *>(a.w + 8 * ch + 4);
-          u[c][0] = w0.x; u[c][1] = w0.y; u[c][2] = w0.z; u[c][3] = w0.w;
-          u[c][4] = w1.x; u[c][5] = w1.y; u[c][6] = w1.z; u[c][7] = w1.w;
+          float4 w0 = *reinterpret_cast<const float4 *>(a.w + 8 * ch);
+          float4 w1 = *reinterpret_cast<const float4 *>(a.w + 8 * ch + 4);
           if (a.phi_t) {
             const float *pp = a.phi_t + (size_t)b * a.C + 8 * ch;
             const float4 p0 = *reinterpret_cast<const float4 *>(pp);
             const float4 p1 = *reinterpret_cast<const float4 *>(pp + 4);
-            u[c][0] += p0.x; u[c][1] += p0.y; u[c][2] += p0.z; u[c][3] += p0.w;
-            u[c][4] += p1.x; u[c][5] += p1.y; u[c][6] += p1.z; u[c][7] += p1.w;
+            w0.x += p0.x; w0.y += p0.y; w0.z += p0.z; w0.w += p0.w;
+            w1.x += p1.x; w1.y += p1.y; w1.z += p1.z; w1.w += p1.w;
           }
+          *reinterpret_cast<float4 *>(ul + 8 * ch) = w0;
+          *reinterpret_cast<float4 *>(ul + 8 * ch + 4) = w1;
         }
       }
+      wave_lds_fence();
     }
     const size_t row = (size_t)tok * a.C;
 
@@ -184,10 +189,13 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
             if (i < kKeep) held[i < kKeep ? i : 0][c] = ck;
             float x[8];
             E::unpack(ck, x);
+            const f32x4_t u0 = *reinterpret_cast<const f32x4_t *>(ul + 8 * ch);
+            const f32x4_t u1 = *reinterpret_cast<const f32x4_t *>(ul + 8 * ch + 4);
+            const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
               ss += x[t] * x[t];
-              dot += u[c][t] * x[t];
+              dot += uu[t] * x[t];
             }
           }
         }
@@ -254,7 +262,8 @@ template <bool kBF16, int CHL, int kKeep, int SMAX>
 hipError_t launch_kernel(const RouteArgs &a, hipStream_t stream) {
   static const int per_cu = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, route_kernel<kBF16, CHL, kKeep, SMAX>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, route_kernel<kBF16, CHL, kKeep, SMAX>, 256,
+                                                     4 * 512 * CHL * sizeof(float)) != hipSuccess ||
         n < 1)
       n = 1;
     return n;
@@ -265,7 +274,8 @@ hipError_t launch_kernel(const RouteArgs &a, hipStream_t stream) {
     cus = 1;
   const long long tokens = (long long)a.B * a.T;
   const long long wgs = std::min<long long>((tokens + 3) / 4, (long long)per_cu * cus);
-  hipLaunchKernelGGL((route_kernel<kBF16, CHL, kKeep, SMAX>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((route_kernel<kBF16, CHL, kKeep, SMAX>), dim3((unsigned)wgs), dim3(256),
+                     4 * (size_t)a.C * sizeof(float), stream, a);
   return hipGetLastError();
 }
 
