@@ -361,7 +361,36 @@ def main() -> int:
             "algorithmic_bytes": bw_bytes, "schedule_bytes": bw_sched,
             "schedule_gbs": bw_sched / (bw_ms * 1e-3) / 1e9}
         log(f"[bench] backward 720p/5s: {bw_ms:.3f} ms")
-        del bws, bouts, bdo
+        # the same gradients given the forward's state (hla_linear_attn_chunked with chunk = N returns it):
+        # the first state build is skipped, K and V are read once fewer
+        bkv = torch.empty((w0.B, w0.H, w0.D, w0.D), dtype=torch.float32, device="cuda")
+        bks = torch.empty((w0.B, w0.H, w0.D), dtype=torch.float32, device="cuda")
+        hla.hla_linear_attn_chunked(bx["q"], bx["k"], bx["v"], w0.N, bx["g"], bx["rope"], w0.eps, kv_out=bkv,
+                                    ksum_out=bks)
+
+        def bwd_saved_call():
+            hla.hla_linear_attn_backward_saved(bx["q"], bx["k"], bx["v"], bkv, bks, bdo, bx["g"], bx["rope"], w0.eps,
+                                               dq=bouts[0], dk=bouts[1], dv=bouts[2], dg=bouts[3], ws=bws)
+
+        bwd_saved_call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            bwd_saved_call()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        bs_ms = float(np.mean(times))
+        bs_sched = bw_sched - tokh * 64 * 2 * 2
+        out["legs"]["backward_saved_720p5s"] = {
+            "N": w0.N, "ms": bs_ms, "tokens_per_s": w0.B * w0.N / (bs_ms * 1e-3),
+            "hbm_gbs": bw_bytes / (bs_ms * 1e-3) / 1e9, "hbm_frac": bw_bytes / (bs_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": bw_bytes, "schedule_bytes": bs_sched,
+            "schedule_gbs": bs_sched / (bs_ms * 1e-3) / 1e9}
+        log(f"[bench] backward from the saved state 720p/5s: {bs_ms:.3f} ms")
+        del bws, bouts, bdo, bkv, bks
 
     # ---------------- anchor backward leg: gradients of the 720p/5s anchor (gated)
     if not args.no_legs:

@@ -13,7 +13,9 @@
  *                            the tokens before it, plus a carried state.
  *   hla_linear_attn_backward, hla_linear_attn_chunked_backward
  *                            gradients of the bidirectional and block-causal
- *                            variants (inputs, gate and carried state).
+ *                            variants (inputs, gate and carried state);
+ *                            hla_linear_attn_backward_saved takes the
+ *                            forward's state instead of rebuilding it.
  *   hla_softmax_anchor       gated non-causal softmax attention (the periodic
  *                            full-rank anchor layer); hla_softmax_anchor_lse
  *                            also writes each row's normaliser.
@@ -194,6 +196,25 @@ hla_status hla_linear_attn_backward(hla_dtype dt, int B, int N, int H, int D,
                                     const hla_rope3d *rope, float eps, const void *dO,
                                     void *dq, void *dk, void *dv, void *dg,
                                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hla_linear_attn_backward given the forward's state instead of rebuilding it:
+ * kv[(b*H + h)][d][e] = sum_j c_j[d] v_j[e] and ksum[(b*H + h)][d] = sum_j relu(k_j)[d]
+ * over the whole sequence (c_j the rotated relu(k_j), as in hla_linear_attn), float,
+ * [B][H][D][D] and [B][H][D], as hla_linear_attn_chunked writes them to kv_out and
+ * ksum_out for chunk_tokens = N and no carried state (that call's o equals
+ * hla_linear_attn's bit for bit). The first state build of the backward is then
+ * skipped; with that state the results are bitwise those of
+ * hla_linear_attn_backward. Arguments and workspace otherwise as
+ * hla_linear_attn_backward.
+ * Errors: as hla_linear_attn_backward, plus INVALID_ARG for a null kv or ksum.
+ */
+hla_status hla_linear_attn_backward_saved(hla_dtype dt, int B, int N, int H, int D,
+                                          const void *q, const void *k, const void *v, const void *g,
+                                          const hla_rope3d *rope, float eps,
+                                          const float *kv, const float *ksum, const void *dO,
+                                          void *dq, void *dk, void *dv, void *dg,
+                                          void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Gradients of hla_linear_attn_chunked (bf16), including the carried and the

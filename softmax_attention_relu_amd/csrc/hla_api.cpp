@@ -89,7 +89,8 @@ hla_status linear_bwd_common(hla_dtype dt, int B, int N, int H, int D, int chunk
                              const void *k, const void *v, const void *g, const hla_rope3d *rope, float eps,
                              const float *kv_in, const float *ksum_in, const void *dO, const float *dkv_out,
                              const float *dksum_out, void *dq, void *dk, void *dv, void *dg, float *dkv_in,
-                             float *dksum_in, void *ws, size_t ws_bytes, hipStream_t stream) {
+                             float *dksum_in, void *ws, size_t ws_bytes, hipStream_t stream,
+                             const float *kv_saved = nullptr, const float *ksum_saved = nullptr) {
   if (!q || !k || !v || !dO || !dq || !dk || !dv) return HLA_ERR_INVALID_ARG;
   if ((g == nullptr) != (dg == nullptr)) return HLA_ERR_INVALID_ARG;
   if (!shape_ok(B, N, H) || chunk_tokens <= 0) return HLA_ERR_INVALID_ARG;
@@ -125,6 +126,8 @@ hla_status linear_bwd_common(hla_dtype dt, int B, int N, int H, int D, int chunk
   a.dkv_in = dkv_in;
   a.dksum_in = dksum_in;
   a.ws = ws;
+  a.kv_saved = kv_saved;
+  a.ksum_saved = ksum_saved;
   return launch_linear_backward(a, plan, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
 }
 
@@ -222,6 +225,15 @@ hla_status hla_linear_attn_backward(hla_dtype dt, int B, int N, int H, int D, co
                                     hipStream_t stream) {
   return linear_bwd_common(dt, B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, dO, nullptr,
                            nullptr, dq, dk, dv, dg, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+hla_status hla_linear_attn_backward_saved(hla_dtype dt, int B, int N, int H, int D, const void *q, const void *k,
+                                          const void *v, const void *g, const hla_rope3d *rope, float eps,
+                                          const float *kv, const float *ksum, const void *dO, void *dq, void *dk,
+                                          void *dv, void *dg, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!kv || !ksum) return HLA_ERR_INVALID_ARG;
+  return linear_bwd_common(dt, B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, dO, nullptr,
+                           nullptr, dq, dk, dv, dg, nullptr, nullptr, ws, ws_bytes, stream, kv, ksum);
 }
 
 size_t hla_linear_attn_chunked_backward_workspace(int B, int N, int H, int D, int chunk_tokens) {

@@ -100,6 +100,9 @@ struct LinearBwdArgs {
   void *dq, *dk, *dv, *dg;
   float *dkv_in, *dksum_in;        // nullable gradient of the carried state
   void *ws;
+  // bidirectional only, nullable: the forward's state over the whole sequence
+  // ([B*H][D][D] and [B*H][D]); given, the first state build is skipped
+  const float *kv_saved = nullptr, *ksum_saved = nullptr;
 };
 
 LinearPlan plan_linear_backward(int B, int N, int H, int chunk_tokens);

@@ -491,8 +491,21 @@ hipError_t launch_linear_backward(const LinearBwdArgs &a, const LinearPlan &p, h
   s.reverse = false;
   s.init_copy = nullptr;
   float *state = nullptr;
-  hipError_t e = launch_state_sums(HLA_BF16, s, p, a.ws, stream, &state);
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (a.kv_saved) {
+    // the forward's state, packed into the one record per head of the prefix
+    // ([D*D state | D key sum]) that the build and scan would have written
+    state = reinterpret_cast<float *>(ws + p.prefix_offset);
+    const size_t heads = (size_t)a.B * a.H;
+    e = hipMemcpy2DAsync(state, kStateFloats * sizeof(float), a.kv_saved, kD * kD * sizeof(float),
+                         kD * kD * sizeof(float), heads, hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return e;
+    e = hipMemcpy2DAsync(state + kD * kD, kStateFloats * sizeof(float), a.ksum_saved, kD * sizeof(float),
+                         kD * sizeof(float), heads, hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return e;
+  } else if ((e = launch_state_sums(HLA_BF16, s, p, a.ws, stream, &state)) != hipSuccess) {
+    return e;
+  }
 
   BwdArgs qa;
   qa.x0 = reinterpret_cast<const uint16_t *>(a.q);

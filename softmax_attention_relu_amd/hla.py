@@ -33,6 +33,7 @@ EXPORTS = (
     "hla_linear_attn_causal",
     "hla_linear_attn_backward_workspace",
     "hla_linear_attn_backward",
+    "hla_linear_attn_backward_saved",
     "hla_linear_attn_chunked_backward_workspace",
     "hla_linear_attn_chunked_backward",
     "hla_softmax_anchor_workspace",
@@ -96,6 +97,11 @@ def lib() -> ctypes.CDLL:
                                                c_void_p, POINTER(hla_rope3d), c_float, c_void_p, c_void_p, c_void_p,
                                                c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.hla_linear_attn_backward.restype = c_int
+        L.hla_linear_attn_backward_saved.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                                                     c_void_p, c_void_p, POINTER(hla_rope3d), c_float, c_void_p,
+                                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                     c_void_p, c_size_t, c_void_p]
+        L.hla_linear_attn_backward_saved.restype = c_int
         L.hla_linear_attn_chunked_backward_workspace.argtypes = [c_int, c_int, c_int, c_int, c_int]
         L.hla_linear_attn_chunked_backward_workspace.restype = c_size_t
         L.hla_linear_attn_chunked_backward.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
@@ -294,6 +300,28 @@ def hla_linear_attn_causal(q, k, v, g=None, rope: Rope3D | None = None, eps: flo
 
 def hla_linear_attn_backward_workspace(B: int, N: int, H: int, D: int = 64) -> int:
     return int(lib().hla_linear_attn_backward_workspace(B, N, H, D))
+
+
+def hla_linear_attn_backward_saved(q, k, v, kv, ksum, do, g=None, rope: Rope3D | None = None, eps: float = 1e-6,
+                                   dq=None, dk=None, dv=None, dg=None, ws=None, stream=None):
+    """Gradients of the bidirectional linear attention (bf16) given the forward's state kv (B, H, D, D) and
+    ksum (B, H, D), as hla_linear_attn_chunked returns for chunk_tokens = N; returns (dq, dk, dv, dg)."""
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    if tuple(kv.shape) != (B, H, D, D) or tuple(ksum.shape) != (B, H, D) or kv.dtype != torch.float32 \
+            or ksum.dtype != torch.float32:
+        raise ValueError("kv must be float32 (B, H, D, D) and ksum float32 (B, H, D)")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if g is not None and dg is None:
+        dg = torch.empty_like(g)
+    ws, nbytes = _workspace(hla_linear_attn_backward_workspace(B, N, H, D), q.device, ws)
+    st = lib().hla_linear_attn_backward_saved(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                              _rope_ptr(rope), float(eps), _ptr(kv), _ptr(ksum), _ptr(do), _ptr(dq),
+                                              _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "hla_linear_attn_backward_saved")
+    return dq, dk, dv, dg
 
 
 def hla_linear_attn_backward(q, k, v, do, g=None, rope: Rope3D | None = None, eps: float = 1e-6, dq=None, dk=None,

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     assert sorted(hla.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
@@ -245,6 +245,20 @@ def test_anchor_saved_forward_validation(L):
     assert bwd(g=FAKE) == E.HLA_ERR_INVALID_ARG
     assert bwd(N=0) == E.HLA_ERR_INVALID_ARG
     assert bwd(ws_bytes=1024) == E.HLA_ERR_WORKSPACE
+
+
+def test_linear_backward_saved_validation(L):
+    """hla_linear_attn_backward_saved rejects a missing kv or ksum before anything else is reached."""
+    E = hla
+
+    def call(kv=FAKE, ksum=FAKE, dO=FAKE, ws_bytes=1 << 40):
+        return L.hla_linear_attn_backward_saved(0, 1, 8, 1, 64, FAKE, FAKE, FAKE, None, None, 1e-6, kv, ksum, dO,
+                                                FAKE, FAKE, FAKE, None, FAKE, ws_bytes, None)
+
+    assert call(kv=None) == E.HLA_ERR_INVALID_ARG
+    assert call(ksum=None) == E.HLA_ERR_INVALID_ARG
+    assert call(dO=None) == E.HLA_ERR_INVALID_ARG
+    assert call(ws_bytes=64) == E.HLA_ERR_WORKSPACE
 
 
 def test_sparse_anchor_validation(L):

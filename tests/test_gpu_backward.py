@@ -134,3 +134,37 @@ def test_backward_full_size_whole_heads():
         ref = oracle.linear_attention_backward(f["q"], f["k"], f["v"], f["do"], f["g"], rope)
         for nm, got, r in zip(("dq", "dk", "dv", "dg"), (dq, dk, dv, dg), ref):
             check(f"{nm} head {h}", host(got[:, :, h:h + 1]), r)
+
+
+@pytest.mark.parametrize("N,bands,gated", [(100, ALIGNED, True), (300, None, False), (1000, UNALIGNED, True),
+                                           (75600, ALIGNED, True)])
+def test_backward_from_saved_state(N, bands, gated):
+    """hla_linear_attn_backward_saved with the state that hla_linear_attn_chunked returns for chunk = N:
+    bitwise equal to hla_linear_attn_backward (same state, same kernels afterwards); on one small shape also
+    against the oracle. N = 75600 is the 720p/5s layer (B1 H32)."""
+    big = N == 75600
+    B, H = (1, 32) if big else (2, 3)
+    grid = (21, 45, 80) if big else GRIDS[N]
+    x = inputs(850 + N, B, N, H, gated)
+    d = {k: dev(v) for k, v in x.items()}
+    rope = None if bands is None else hla.Rope3D(grid, bands)
+    say(f"[bwd saved] N={N} B={B} H={H} bands={bands} gated={gated}")
+    kv = torch.empty((B, H, 64, 64), dtype=torch.float32, device="cuda")
+    ks = torch.empty((B, H, 64), dtype=torch.float32, device="cuda")
+    o_chunk = hla.hla_linear_attn_chunked(d["q"], d["k"], d["v"], N, d.get("g"), rope, kv_out=kv, ksum_out=ks)
+    o_plain = hla.hla_linear_attn(d["q"], d["k"], d["v"], d.get("g"), rope)
+    saved = hla.hla_linear_attn_backward_saved(d["q"], d["k"], d["v"], kv, ks, d["do"], d.get("g"), rope)
+    full = hla.hla_linear_attn_backward(d["q"], d["k"], d["v"], d["do"], d.get("g"), rope)
+    torch.cuda.synchronize()
+    assert torch.equal(o_chunk, o_plain)
+    for nm, a, b in zip(("dq", "dk", "dv", "dg"), saved, full):
+        if b is None:
+            assert a is None
+            continue
+        assert torch.equal(a, b), nm
+    if N == 100:
+        f = {k: synth.to_f64(v) for k, v in x.items()}
+        ref = oracle.linear_attention_backward(f["q"], f["k"], f["v"], f["do"], f.get("g"),
+                                               oracle.Rope3D(grid, bands))
+        for nm, got, r in zip(("dq", "dk", "dv", "dg"), saved, ref):
+            check(f"saved {nm}", host(got), r)
