@@ -65,7 +65,7 @@ extern "C" {
 typedef enum {
   HLA_OK = 0,
   HLA_ERR_INVALID_ARG = 1, /* null required pointer, bad size, inconsistent shapes */
-  HLA_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (D != 64, ...) */
+  HLA_ERR_UNSUPPORTED = 2, /* a valid request the library does not implement (D != 64, ...) */
   HLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace query */
   HLA_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError) */
 } hla_status;
