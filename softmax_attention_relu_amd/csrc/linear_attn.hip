@@ -422,22 +422,61 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
   const int nsl = a.n_chunks * a.slabs_per_chunk;
   const float *p = a.part + (size_t)bh * nsl * kStateFloats + idx;
   float *pre = a.prefix + (size_t)bh * a.n_chunks * kStateFloats + idx;
-  for (int ci = 0; ci < a.n_chunks; ++ci) {
-    const int c = a.reverse ? a.n_chunks - 1 - ci : ci;
-    // slabs are added in index order; the loads are issued eight at a time
-    const float *pc = p + (size_t)c * a.slabs_per_chunk * kStateFloats;
+  // Slabs are summed in index order from zero, then added to the running state,
+  // chunk by chunk in scan order. With eight or more slabs per chunk their loads
+  // go out eight at a time with no store between them. With fewer, the (chunk,
+  // slab) partials are loaded eight at a time across chunks before any of them
+  // is added: a prefix store could otherwise be taken to alias the next chunk's
+  // partials, one memory round trip per chunk.
+  const int spc = a.slabs_per_chunk;
+  if (spc >= 8) {
+    for (int ci = 0; ci < a.n_chunks; ++ci) {
+      const int c = a.reverse ? a.n_chunks - 1 - ci : ci;
+      const float *pc = p + (size_t)c * spc * kStateFloats;
+      float s = 0.f;
+      int i = 0;
+      for (; i + 8 <= spc; i += 8) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = pc[(size_t)(i + j) * kStateFloats];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += x[j];
+      }
+      for (; i < spc; ++i) s += pc[(size_t)i * kStateFloats];
+      run += s;
+      pre[(size_t)c * kStateFloats] = run;
+    }
+  } else {
+    int lc = 0, ls = 0;  // next partial to load: chunk (scan order), slab
+    int sc = 0, ss = 0;  // next partial to add
     float s = 0.f;
-    int i = 0;
-    for (; i + 8 <= a.slabs_per_chunk; i += 8) {
+    for (int t0 = 0; t0 < nsl; t0 += 8) {
       float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = pc[(size_t)(i + j) * kStateFloats];
+      for (int j = 0; j < 8; ++j) {
+        // past the end: a repeat of the last partial, never added
+        const int ci = min(lc, a.n_chunks - 1);
+        const int c = a.reverse ? a.n_chunks - 1 - ci : ci;
+        x[j] = p[((size_t)c * spc + (lc < a.n_chunks ? ls : spc - 1)) * kStateFloats];
+        if (++ls == spc) {
+          ls = 0;
+          ++lc;
+        }
+      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s += x[j];
+      for (int j = 0; j < 8; ++j)
+        if (t0 + j < nsl) {
+          s += x[j];
+          if (++ss == spc) {
+            const int c = a.reverse ? a.n_chunks - 1 - sc : sc;
+            run += s;
+            pre[(size_t)c * kStateFloats] = run;
+            s = 0.f;
+            ss = 0;
+            ++sc;
+          }
+        }
     }
-    for (; i < a.slabs_per_chunk; ++i) s += pc[(size_t)i * kStateFloats];
-    run += s;
-    pre[(size_t)c * kStateFloats] = run;
   }
   if (a.kv_out) {
     if (idx < kD * kD)
@@ -883,7 +922,7 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
   __shared__ __align__(16) float z_all[kHeadsPerWG][kD];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: head and bases in scalar registers
   const int half = lane >> 5, tl = lane & 31;
   const int hgroup = blockIdx.x % a.ngroups;
   const int rng = blockIdx.x / a.ngroups;
@@ -931,26 +970,43 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
   const size_t head_base = (size_t)b * a.N * tok_stride + (size_t)h * kD;
   const int kp_self = key_perm(tl);
 
-  // v rows of the next step are loaded one step ahead (right after this step's
-  // V^T is in LDS), so a step does not start by waiting for them
-  uint4 vnext[4];
-  {
-    const int hi0 = min(hi_r, lo + kApplySub);
-    const size_t row0 = head_base + (size_t)min(lo + tl, hi0 - 1) * tok_stride;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) vnext[s] = *reinterpret_cast<const uint4 *>(a.v + row0 + 16 * s + 8 * half);
-  }
   for (int sub = lo; sub < hi_r; sub += kApplySub) {
     const int hi = min(hi_r, sub + kApplySub);
     const int n = sub + tl;
     const bool valid = n < hi;
-    const size_t row = head_base + (size_t)min(n, hi - 1) * tok_stride;
+    // the step's rows: a wave-uniform base plus one 32-bit byte offset per lane,
+    // shared by q, k, v, g and o (one layout); keeps 64-bit lane addresses out
+    // of the step's registers
+    const size_t step_base = head_base + (size_t)sub * tok_stride;
+    const uint32_t roff = (uint32_t)(min(n, hi - 1) - sub) * (uint32_t)(tok_stride * sizeof(uint16_t));
+    auto at = [&](const uint16_t *base, int d) {
+      return reinterpret_cast<const char *>(base + step_base) + roff + d * sizeof(uint16_t);
+    };
 
-    // v as 16-byte pieces; q and k are read per reduction step below, in the
-    // state's dim order (8-byte pieces)
+    // Every global read of the step is issued here, before any of them is
+    // used (v as 16-byte pieces; q and k as 8-byte pieces in the state's dim
+    // order, per reduction step; the gate pieces of the output): the step
+    // waits for one memory round trip instead of one per reduction step, one
+    // for the gate and one for its first V^T write.
     uint4 vp[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) vp[s] = vnext[s];
+    for (int s = 0; s < 4; ++s) vp[s] = *reinterpret_cast<const uint4 *>(at(a.v, 16 * s + 8 * half));
+    uint2 qkp[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int d0 = 32 * (st >> 1) + 16 * (st & 1) + 4 * half;
+      qkp[st][0] = *reinterpret_cast<const uint2 *>(at(a.q, d0));
+      qkp[st][1] = *reinterpret_cast<const uint2 *>(at(a.q, d0 + 8));
+      qkp[st][2] = *reinterpret_cast<const uint2 *>(at(a.k, d0));
+      qkp[st][3] = *reinterpret_cast<const uint2 *>(at(a.k, d0 + 8));
+    }
+    uint2 gws[2][4];
+    if constexpr (kGate) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gws[mb][i] = *reinterpret_cast<const uint2 *>(at(a.g, 32 * mb + 8 * i + 4 * half));
+    }
     TokenPos tp;
     if constexpr (kRope) tp = token_pos(a.rope, (uint32_t)min(n, hi - 1));
     if (!valid) {
@@ -967,14 +1023,6 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
         vt[(16 * s + 8 * half + t) * kCtRow + kp_self] = (uint16_t)((t & 1) ? (w[t >> 1] >> 16) : (w[t >> 1] & 0xFFFFu));
     }
 
-    if (sub + kApplySub < hi_r) {
-      const int nn = sub + kApplySub + tl;
-      const int hin = min(hi_r, sub + 2 * kApplySub);
-      const size_t rown = head_base + (size_t)min(nn, hin - 1) * tok_stride;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) vnext[s] = *reinterpret_cast<const uint4 *>(a.v + rown + 16 * s + 8 * half);
-    }
-
     f32x16_t tacc, uacc, oacc[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -989,10 +1037,7 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
       const int kb = st >> 1, s2 = st & 1;
       const int d0 = 32 * kb + 16 * s2 + 4 * half;
       float fq[8], fk[8];
-      uint2 q0 = *reinterpret_cast<const uint2 *>(a.q + row + d0);
-      uint2 q1 = *reinterpret_cast<const uint2 *>(a.q + row + d0 + 8);
-      uint2 k0 = *reinterpret_cast<const uint2 *>(a.k + row + d0);
-      uint2 k1 = *reinterpret_cast<const uint2 *>(a.k + row + d0 + 8);
+      uint2 q0 = qkp[st][0], q1 = qkp[st][1], k0 = qkp[st][2], k1 = qkp[st][3];
       if (!valid) q0 = q1 = k0 = k1 = make_uint2(0, 0);
       const uint32_t qw[4] = {q0.x, q0.y, q1.x, q1.y};
       const uint32_t kw[4] = {k0.x, k0.y, k1.x, k1.y};
@@ -1144,23 +1189,13 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
           sacc[kb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cta[kb], vtb[nb], sacc[kb][nb], 0, 0, 0);
     }
 
-    // normalise, gate, store: lane holds dims 32*mb + 8i + 4*half + j of token n.
-    // The gate pieces are all loaded before the first store (a store to o
-    // could otherwise be taken to alias the next gate load, one round trip each).
+    // normalise, gate, store: lane holds dims 32*mb + 8i + 4*half + j of token n
     const float inv = 1.f / den;
     if (valid) {
-      uint2 gws[2][4];
-      if constexpr (kGate) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gws[mb][i] = *reinterpret_cast<const uint2 *>(a.g + row + 32 * mb + 8 * i + 4 * half);
-      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const size_t off = row + 32 * mb + 8 * i + 4 * half;
           float y[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) y[j] = oacc[mb][4 * i + j] * inv;
@@ -1171,7 +1206,8 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
             y[2] *= sigmoid_fast(bf16_lo(gw.y));
             y[3] *= sigmoid_fast(bf16_hi(gw.y));
           }
-          *reinterpret_cast<uint2 *>(a.o + off) = make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
+          *reinterpret_cast<uint2 *>(const_cast<char *>(at(a.o, 32 * mb + 8 * i + 4 * half))) =
+              make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
         }
     }
     wave_lds_fence();  // the next step's LDS writes come after these reads
