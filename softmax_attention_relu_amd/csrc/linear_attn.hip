@@ -425,7 +425,7 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
   // Slabs are summed in index order from zero, then added to the running state,
   // chunk by chunk in scan order. With eight or more slabs per chunk their loads
   // go out eight at a time with no store between them. With fewer, the (chunk,
-  // slab) partials are loaded eight at a time across chunks before any of them
+  // slab) partials are loaded sixteen at a time across chunks before any of them
   // is added: a prefix store could otherwise be taken to alias the next chunk's
   // partials, one memory round trip per chunk.
   const int spc = a.slabs_per_chunk;
@@ -450,10 +450,10 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
     int lc = 0, ls = 0;  // next partial to load: chunk (scan order), slab
     int sc = 0, ss = 0;  // next partial to add
     float s = 0.f;
-    for (int t0 = 0; t0 < nsl; t0 += 8) {
-      float x[8];
+    for (int t0 = 0; t0 < nsl; t0 += 16) {
+      float x[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 16; ++j) {
         // past the end: a repeat of the last partial, never added
         const int ci = min(lc, a.n_chunks - 1);
         const int c = a.reverse ? a.n_chunks - 1 - ci : ci;
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 16; ++j)
         if (t0 + j < nsl) {
           s += x[j];
           if (++ss == spc) {
