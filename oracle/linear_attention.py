@@ -41,44 +41,56 @@ def _sigmoid(x: np.ndarray) -> np.ndarray:
 
 
 def _features(q, k, rope: Rope3D | None):
-    """phi(Q), phi(K) and their rotated forms (pseudocode steps 1 and 2)."""
-    q_relu = np.maximum(q, 0.0)
-    k_relu = np.maximum(k, 0.0)
+    """Feature maps of the queries and keys: (phi(q), phi(k), R phi(q), R phi(k)).
+
+    phi is the ReLU; R is the 3D rotation of each token, applied after phi. The
+    unrotated features feed the denominator, the rotated ones the numerator.
+    """
+    pos_q = np.maximum(q, 0.0)
+    pos_k = np.maximum(k, 0.0)
     if rope is None:
-        return q_relu, k_relu, q_relu, k_relu
+        return pos_q, pos_k, pos_q, pos_k
     if rope.n_tokens != q.shape[1]:
         raise ValueError("RoPE grid does not match the token count")
     theta = rope3d_angles(rope)
-    return q_relu, k_relu, rope3d_rotate(q_relu, theta), rope3d_rotate(k_relu, theta)
+    return pos_q, pos_k, rope3d_rotate(pos_q, theta), rope3d_rotate(pos_k, theta)
 
 
 def linear_attention(q, k, v, g=None, rope: Rope3D | None = None, eps: float = 1e-6,
                      rows=None, return_state: bool = False):
     """Bidirectional linear attention of (B, N, H, D) inputs, fp64.
 
+    For every batch b and head h the D x D state is the sum over all tokens of
+    the outer products c_j^T v_j (c_j the rotated key features), formed as one
+    product of the stacked rows, and the key sum adds the unrotated features.
+    Each requested row then reads both: o_i = (a_i S) / (phi(q_i) . z + eps),
+    and the gate multiplies in last.
+
     ``rows`` optionally selects the token indices whose outputs are returned
     (the state always sums over all N tokens). With ``return_state`` the
     (KV, ksum) pair of shape (B, H, D, D) and (B, H, D) is returned as well.
     """
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
-    q_relu, k_relu, q_rope, k_rope = _features(q, k, rope)
-
-    # step 3: numerator with RoPE on both sides
-    kv = np.einsum("bnhd,bnhe->bhde", k_rope, v)
-    # step 4: denominator without RoPE
-    k_sum = k_relu.sum(axis=1)
-    if rows is not None:
-        rows = np.asarray(rows)
-        q_rope, q_relu = q_rope[:, rows], q_relu[:, rows]
-        g = None if g is None else g[:, rows]
-    numerator = np.einsum("bnhd,bhde->bnhe", q_rope, kv)
-    denominator = np.einsum("bnhd,bhd->bnh", q_relu, k_sum)
-    # step 5: normalise, then gate
-    out = numerator / (denominator[..., None] + eps)
+    B, N, H, D = q.shape
+    phi_q, phi_k, rot_q, rot_k = _features(q, k, rope)
+    sel = np.arange(N) if rows is None else np.asarray(rows)
+    state = np.zeros((B, H, D, D))
+    zsum = np.zeros((B, H, D))
+    out = np.zeros((B, len(sel), H, D))
+    for b in range(B):
+        for h in range(H):
+            c = rot_k[b, :, h, :]
+            state[b, h] = c.T @ v[b, :, h, :]
+            zsum[b, h] = phi_k[b, :, h, :].sum(axis=0)
+            # per-row products as plain sums, so a row's value does not depend
+            # on which other rows are requested
+            num = np.einsum("id,de->ie", rot_q[b, sel, h, :], state[b, h])
+            den = np.einsum("id,d->i", phi_q[b, sel, h, :], zsum[b, h]) + eps
+            out[b, :, h, :] = num / den[:, None]
     if g is not None:
-        out = _sigmoid(g) * out
+        out = _sigmoid(g[:, sel]) * out
     if return_state:
-        return out, kv, k_sum
+        return out, state, zsum
     return out
 
 

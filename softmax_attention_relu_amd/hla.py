@@ -182,23 +182,98 @@ def _dtype_code(t) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
-def _stream(stream) -> int | None:
+def _stream_obj(stream):
+    """The torch stream the call runs on (a torch stream, a raw HIP stream handle, or None for current)."""
     torch = _torch()
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream()
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
 
 
 def _bnhd(q):
+    torch = _torch()
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q: expected a torch.Tensor")
     if q.dim() != 4:
-        raise ValueError("expected a (B, N, H, D) tensor")
+        raise ValueError("q: expected a (B, N, H, D) tensor")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"q: unsupported dtype {q.dtype}")
     return tuple(int(x) for x in q.shape)
+
+
+class _Checks:
+    """Shape, dtype and device checks of every tensor argument, before any call into the library.
+
+    The kernels read and write through raw pointers, so a tensor of the wrong
+    shape or dtype would be read or written out of bounds; every mismatch is a
+    ValueError raised here instead. All shapes and dtypes are checked first,
+    then that every tensor is a contiguous device tensor on one device.
+    """
+
+    def __init__(self):
+        self._items = []
+
+    def add(self, name, t, shape, dtype, optional=True):
+        if t is None:
+            if not optional:
+                raise ValueError(f"{name} is required")
+            return self
+        self._items.append((name, t, tuple(shape), dtype))
+        return self
+
+    def run(self):
+        torch = _torch()
+        for name, t, shape, dtype in self._items:
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name}: expected a torch.Tensor")
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {shape}")
+            if t.dtype != dtype:
+                raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        dev = None
+        for name, t, _, _ in self._items:
+            if not t.is_cuda:
+                raise ValueError(f"{name}: libhla takes device tensors")
+            if not t.is_contiguous():
+                raise ValueError(f"{name}: libhla takes contiguous tensors")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{name}: on {t.device}, the other tensors on {dev}")
+
+
+def _check_rope(rope, N: int, D: int, device=None):
+    """A Rope3D's grid must cover the N tokens and its tables must match its grid and bands (and, when
+    ``device`` is given, sit on it)."""
+    if rope is None:
+        return
+    if not isinstance(rope, Rope3D):
+        raise TypeError("rope: expected a Rope3D")
+    T, Hg, Wg = rope.grid
+    if T * Hg * Wg != N:
+        raise ValueError(f"rope: grid {rope.grid} covers {T * Hg * Wg} tokens, the call has {N}")
+    if sum(rope.bands) != D:
+        raise ValueError(f"rope: bands {rope.bands} do not sum to D = {D}")
+    torch = _torch()
+    for nm, tab, n, d in zip("thw", rope.tables, rope.grid, rope.bands):
+        if d == 0:
+            continue
+        if tuple(tab.shape) != (n, d // 2, 2) or tab.dtype != torch.float32:
+            raise ValueError(f"rope: the {nm} table is {tuple(tab.shape)} {tab.dtype}, expected ({n}, {d // 2}, 2) "
+                             "float32")
+        if device is not None and (not tab.is_cuda or tab.device != device or not tab.is_contiguous()):
+            raise ValueError(f"rope: the {nm} table must be a contiguous tensor on {device}")
 
 
 def _workspace(nbytes: int, device, ws):
     torch = _torch()
     if ws is None:
         ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    else:
+        if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous() or ws.device != device:
+            raise ValueError(f"ws: expected a contiguous device tensor on {device}")
     return ws, ws.numel() * ws.element_size()
 
 
@@ -242,6 +317,25 @@ def _rope_ptr(rope):
 
 # ----------------------------------------------------------------------------
 # entry points
+#
+# Every function checks each tensor argument's shape, dtype and device against
+# q (or the router's first source) before calling into the library, and
+# allocates what it returns and any workspace on the stream the call runs on.
+
+def _like(chk: _Checks, ref, **named):
+    """Register tensors that must have q's shape and dtype."""
+    for name, t in named.items():
+        chk.add(name, t, ref.shape, ref.dtype)
+    return chk
+
+
+def _state(chk: _Checks, B, H, D, **named):
+    """Register fp32 state tensors: the kv ones are (B, H, D, D), the key sums (B, H, D)."""
+    torch = _torch()
+    for name, t in named.items():
+        chk.add(name, t, (B, H, D, D) if "kv" in name else (B, H, D), torch.float32)
+    return chk
+
 
 def hla_linear_attn_workspace(B: int, N: int, H: int, D: int = 64) -> int:
     return int(lib().hla_linear_attn_workspace(B, N, H, D))
@@ -251,12 +345,18 @@ def hla_linear_attn(q, k, v, g=None, rope: Rope3D | None = None, eps: float = 1e
     """Bidirectional ReLU+RoPE linear attention; returns o."""
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    if o is None:
-        o = torch.empty_like(q)
-    ws, nbytes = _workspace(hla_linear_attn_workspace(B, N, H, D), q.device, ws)
-    st = lib().hla_linear_attn(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _rope_ptr(rope),
-                               float(eps), _ptr(o), _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_linear_attn")
+    chk = _like(_Checks(), q, q=q, k=k, v=v, g=g, o=o)
+    _check_rope(rope, N, D)
+    chk.run()
+    _check_rope(rope, N, D, q.device)
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if o is None:
+            o = torch.empty_like(q)
+        ws, nbytes = _workspace(hla_linear_attn_workspace(B, N, H, D), q.device, ws)
+    r = lib().hla_linear_attn(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _rope_ptr(rope),
+                              float(eps), _ptr(o), _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_linear_attn")
     return o
 
 
@@ -269,13 +369,20 @@ def hla_linear_attn_chunked(q, k, v, chunk_tokens: int, g=None, rope: Rope3D | N
     """Block-causal linear attention with carried state; returns o (state goes to kv_out/ksum_out)."""
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    if o is None:
-        o = torch.empty_like(q)
-    ws, nbytes = _workspace(hla_linear_attn_chunked_workspace(B, N, H, D, chunk_tokens), q.device, ws)
-    st = lib().hla_linear_attn_chunked(_dtype_code(q), B, N, H, D, int(chunk_tokens), _ptr(q), _ptr(k), _ptr(v),
-                                       _ptr(g), _rope_ptr(rope), float(eps), _ptr(kv_in), _ptr(ksum_in),
-                                       _ptr(kv_out), _ptr(ksum_out), _ptr(o), _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_linear_attn_chunked")
+    chk = _like(_Checks(), q, q=q, k=k, v=v, g=g, o=o)
+    _state(chk, B, H, D, kv_in=kv_in, ksum_in=ksum_in, kv_out=kv_out, ksum_out=ksum_out)
+    _check_rope(rope, N, D)
+    chk.run()
+    _check_rope(rope, N, D, q.device)
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if o is None:
+            o = torch.empty_like(q)
+        ws, nbytes = _workspace(hla_linear_attn_chunked_workspace(B, N, H, D, chunk_tokens), q.device, ws)
+    r = lib().hla_linear_attn_chunked(_dtype_code(q), B, N, H, D, int(chunk_tokens), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(g), _rope_ptr(rope), float(eps), _ptr(kv_in), _ptr(ksum_in),
+                                      _ptr(kv_out), _ptr(ksum_out), _ptr(o), _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_linear_attn_chunked")
     return o
 
 
@@ -288,18 +395,35 @@ def hla_linear_attn_causal(q, k, v, g=None, rope: Rope3D | None = None, eps: flo
     """Token-causal linear attention (bf16) with optional carried state; returns o."""
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    if o is None:
-        o = torch.empty_like(q)
-    ws, nbytes = _workspace(hla_linear_attn_causal_workspace(B, N, H, D), q.device, ws)
-    st = lib().hla_linear_attn_causal(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                      _rope_ptr(rope), float(eps), _ptr(kv_in), _ptr(ksum_in), _ptr(kv_out),
-                                      _ptr(ksum_out), _ptr(o), _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_linear_attn_causal")
+    chk = _like(_Checks(), q, q=q, k=k, v=v, g=g, o=o)
+    _state(chk, B, H, D, kv_in=kv_in, ksum_in=ksum_in, kv_out=kv_out, ksum_out=ksum_out)
+    _check_rope(rope, N, D)
+    chk.run()
+    _check_rope(rope, N, D, q.device)
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if o is None:
+            o = torch.empty_like(q)
+        ws, nbytes = _workspace(hla_linear_attn_causal_workspace(B, N, H, D), q.device, ws)
+    r = lib().hla_linear_attn_causal(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                     _rope_ptr(rope), float(eps), _ptr(kv_in), _ptr(ksum_in), _ptr(kv_out),
+                                     _ptr(ksum_out), _ptr(o), _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_linear_attn_causal")
     return o
 
 
 def hla_linear_attn_backward_workspace(B: int, N: int, H: int, D: int = 64) -> int:
     return int(lib().hla_linear_attn_backward_workspace(B, N, H, D))
+
+
+def _grad_outputs(q, k, v, g, dq, dk, dv, dg):
+    torch = _torch()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if g is not None and dg is None:
+        dg = torch.empty_like(g)
+    return dq, dk, dv, dg
 
 
 def hla_linear_attn_backward_saved(q, k, v, kv, ksum, do, g=None, rope: Rope3D | None = None, eps: float = 1e-6,
@@ -308,19 +432,20 @@ def hla_linear_attn_backward_saved(q, k, v, kv, ksum, do, g=None, rope: Rope3D |
     ksum (B, H, D), as hla_linear_attn_chunked returns for chunk_tokens = N; returns (dq, dk, dv, dg)."""
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    if tuple(kv.shape) != (B, H, D, D) or tuple(ksum.shape) != (B, H, D) or kv.dtype != torch.float32 \
-            or ksum.dtype != torch.float32:
-        raise ValueError("kv must be float32 (B, H, D, D) and ksum float32 (B, H, D)")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    if g is not None and dg is None:
-        dg = torch.empty_like(g)
-    ws, nbytes = _workspace(hla_linear_attn_backward_workspace(B, N, H, D), q.device, ws)
-    st = lib().hla_linear_attn_backward_saved(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                              _rope_ptr(rope), float(eps), _ptr(kv), _ptr(ksum), _ptr(do), _ptr(dq),
-                                              _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_linear_attn_backward_saved")
+    chk = _like(_Checks(), q, q=q, k=k, v=v, g=g, do=do, dq=dq, dk=dk, dv=dv, dg=dg)
+    chk.add("kv", kv, (B, H, D, D), torch.float32, optional=False)
+    chk.add("ksum", ksum, (B, H, D), torch.float32, optional=False)
+    _check_rope(rope, N, D)
+    chk.run()
+    _check_rope(rope, N, D, q.device)
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv, dg = _grad_outputs(q, k, v, g, dq, dk, dv, dg)
+        ws, nbytes = _workspace(hla_linear_attn_backward_workspace(B, N, H, D), q.device, ws)
+    r = lib().hla_linear_attn_backward_saved(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                             _rope_ptr(rope), float(eps), _ptr(kv), _ptr(ksum), _ptr(do), _ptr(dq),
+                                             _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_linear_attn_backward_saved")
     return dq, dk, dv, dg
 
 
@@ -329,16 +454,18 @@ def hla_linear_attn_backward(q, k, v, do, g=None, rope: Rope3D | None = None, ep
     """Gradients of the bidirectional linear attention (bf16); returns (dq, dk, dv, dg), dg None without g."""
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    if g is not None and dg is None:
-        dg = torch.empty_like(g)
-    ws, nbytes = _workspace(hla_linear_attn_backward_workspace(B, N, H, D), q.device, ws)
-    st = lib().hla_linear_attn_backward(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                        _rope_ptr(rope), float(eps), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
-                                        _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_linear_attn_backward")
+    chk = _like(_Checks(), q, q=q, k=k, v=v, g=g, do=do, dq=dq, dk=dk, dv=dv, dg=dg)
+    _check_rope(rope, N, D)
+    chk.run()
+    _check_rope(rope, N, D, q.device)
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv, dg = _grad_outputs(q, k, v, g, dq, dk, dv, dg)
+        ws, nbytes = _workspace(hla_linear_attn_backward_workspace(B, N, H, D), q.device, ws)
+    r = lib().hla_linear_attn_backward(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _rope_ptr(rope), float(eps), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                       _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_linear_attn_backward")
     return dq, dk, dv, dg
 
 
@@ -356,17 +483,21 @@ def hla_linear_attn_chunked_backward(q, k, v, do, chunk_tokens: int, g=None, rop
     """
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    if g is not None and dg is None:
-        dg = torch.empty_like(g)
-    ws, nbytes = _workspace(hla_linear_attn_chunked_backward_workspace(B, N, H, D, chunk_tokens), q.device, ws)
-    st = lib().hla_linear_attn_chunked_backward(
+    chk = _like(_Checks(), q, q=q, k=k, v=v, g=g, do=do, dq=dq, dk=dk, dv=dv, dg=dg)
+    _state(chk, B, H, D, kv_in=kv_in, ksum_in=ksum_in, dkv_out=dkv_out, dksum_out=dksum_out, dkv_in=dkv_in,
+           dksum_in=dksum_in)
+    _check_rope(rope, N, D)
+    chk.run()
+    _check_rope(rope, N, D, q.device)
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv, dg = _grad_outputs(q, k, v, g, dq, dk, dv, dg)
+        ws, nbytes = _workspace(hla_linear_attn_chunked_backward_workspace(B, N, H, D, chunk_tokens), q.device, ws)
+    r = lib().hla_linear_attn_chunked_backward(
         _dtype_code(q), B, N, H, D, int(chunk_tokens), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _rope_ptr(rope),
         float(eps), _ptr(kv_in), _ptr(ksum_in), _ptr(do), _ptr(dkv_out), _ptr(dksum_out), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(dg), _ptr(dkv_in), _ptr(dksum_in), _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_linear_attn_chunked_backward")
+        _ptr(dv), _ptr(dg), _ptr(dkv_in), _ptr(dksum_in), _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_linear_attn_chunked_backward")
     return dq, dk, dv, dg
 
 
@@ -374,18 +505,24 @@ def hla_softmax_anchor_workspace(B: int, N: int, H: int, D: int = 64) -> int:
     return int(lib().hla_softmax_anchor_workspace(B, N, H, D))
 
 
+def _default_scale(scale, D):
+    return 1.0 / float(D) ** 0.5 if scale is None else scale
+
+
 def hla_softmax_anchor(q, k, v, g=None, scale: float | None = None, o=None, ws=None, stream=None):
     """Gated non-causal softmax attention (bf16); returns o."""
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    if scale is None:
-        scale = 1.0 / float(np.sqrt(D))
-    if o is None:
-        o = torch.empty_like(q)
-    ws, nbytes = _workspace(hla_softmax_anchor_workspace(B, N, H, D), q.device, ws)
-    st = lib().hla_softmax_anchor(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
-                                  _ptr(o), _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_softmax_anchor")
+    scale = _default_scale(scale, D)
+    _like(_Checks(), q, q=q, k=k, v=v, g=g, o=o).run()
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if o is None:
+            o = torch.empty_like(q)
+        ws, nbytes = _workspace(hla_softmax_anchor_workspace(B, N, H, D), q.device, ws)
+    r = lib().hla_softmax_anchor(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
+                                 _ptr(o), _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_softmax_anchor")
     return o
 
 
@@ -394,16 +531,19 @@ def hla_softmax_anchor_lse(q, k, v, g=None, scale: float | None = None, o=None, 
     lse float [B, H, N]."""
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    if scale is None:
-        scale = 1.0 / float(np.sqrt(D))
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    ws, nbytes = _workspace(hla_softmax_anchor_workspace(B, N, H, D), q.device, ws)
-    st = lib().hla_softmax_anchor_lse(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
-                                      _ptr(o), _ptr(lse), _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_softmax_anchor_lse")
+    scale = _default_scale(scale, D)
+    chk = _like(_Checks(), q, q=q, k=k, v=v, g=g, o=o)
+    chk.add("lse", lse, (B, H, N), torch.float32).run()
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        ws, nbytes = _workspace(hla_softmax_anchor_workspace(B, N, H, D), q.device, ws)
+    r = lib().hla_softmax_anchor_lse(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
+                                     _ptr(o), _ptr(lse), _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_softmax_anchor_lse")
     return o, lse
 
 
@@ -416,18 +556,16 @@ def hla_softmax_anchor_backward(q, k, v, do, g=None, scale: float | None = None,
     """Gradients of the gated softmax anchor (bf16); returns (dq, dk, dv, dg), dg None without g."""
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    if scale is None:
-        scale = 1.0 / float(D) ** 0.5
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    if g is not None and dg is None:
-        dg = torch.empty_like(g)
-    ws, nbytes = _workspace(hla_softmax_anchor_backward_workspace(B, N, H, D), q.device, ws)
-    st = lib().hla_softmax_anchor_backward(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                           float(scale), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
-                                           _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_softmax_anchor_backward")
+    scale = _default_scale(scale, D)
+    _like(_Checks(), q, q=q, k=k, v=v, g=g, do=do, dq=dq, dk=dk, dv=dv, dg=dg).run()
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv, dg = _grad_outputs(q, k, v, g, dq, dk, dv, dg)
+        ws, nbytes = _workspace(hla_softmax_anchor_backward_workspace(B, N, H, D), q.device, ws)
+    r = lib().hla_softmax_anchor_backward(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                          float(scale), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                          _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_softmax_anchor_backward")
     return dq, dk, dv, dg
 
 
@@ -437,20 +575,18 @@ def hla_softmax_anchor_backward_saved(q, k, v, o, lse, do, g=None, scale: float 
     hla_softmax_anchor_lse); returns (dq, dk, dv, dg), dg None without g."""
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    if scale is None:
-        scale = 1.0 / float(D) ** 0.5
-    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
-        raise ValueError("lse must be float32 of shape (B, H, N)")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    if g is not None and dg is None:
-        dg = torch.empty_like(g)
-    ws, nbytes = _workspace(hla_softmax_anchor_backward_workspace(B, N, H, D), q.device, ws)
-    st = lib().hla_softmax_anchor_backward_saved(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                                 float(scale), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                                                 _ptr(dv), _ptr(dg), _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_softmax_anchor_backward_saved")
+    scale = _default_scale(scale, D)
+    chk = _like(_Checks(), q, q=q, k=k, v=v, g=g, do=do, dq=dq, dk=dk, dv=dv, dg=dg)
+    chk.add("o", o, q.shape, q.dtype, optional=False)
+    chk.add("lse", lse, (B, H, N), torch.float32, optional=False).run()
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        dq, dk, dv, dg = _grad_outputs(q, k, v, g, dq, dk, dv, dg)
+        ws, nbytes = _workspace(hla_softmax_anchor_backward_workspace(B, N, H, D), q.device, ws)
+    r = lib().hla_softmax_anchor_backward_saved(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                                float(scale), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                                _ptr(dv), _ptr(dg), _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_softmax_anchor_backward_saved")
     return dq, dk, dv, dg
 
 
@@ -467,22 +603,22 @@ def hla_softmax_anchor_block_sparse(q, k, v, blocks, counts, g=None, scale: floa
     """
     torch = _torch()
     B, N, H, D = _bnhd(q)
-    if scale is None:
-        scale = 1.0 / float(D) ** 0.5
+    scale = _default_scale(scale, D)
     nqb = -(-N // SPARSE_Q_BLOCK)
-    if blocks.dtype != torch.int32 or counts.dtype != torch.int32:
-        raise TypeError("blocks and counts must be int32")
-    if tuple(blocks.shape[:3]) != (B, H, nqb) or tuple(counts.shape) != (B, H, nqb) or blocks.dim() != 4:
-        raise ValueError("blocks must be (B, H, ceil(N/128), max_blocks) and counts (B, H, ceil(N/128))")
-    if not (blocks.is_contiguous() and counts.is_contiguous()):
-        raise ValueError("blocks and counts must be contiguous")
-    if o is None:
-        o = torch.empty_like(q)
-    ws, nbytes = _workspace(hla_softmax_anchor_workspace(B, N, H, D), q.device, ws)
-    st = lib().hla_softmax_anchor_block_sparse(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                               float(scale), _ptr(blocks), _ptr(counts), int(blocks.shape[3]),
-                                               _ptr(o), _ptr(ws), nbytes, _stream(stream))
-    _check(st, "hla_softmax_anchor_block_sparse")
+    if not isinstance(blocks, torch.Tensor) or blocks.dim() != 4:
+        raise ValueError("blocks must be a (B, H, ceil(N/128), max_blocks) tensor")
+    chk = _like(_Checks(), q, q=q, k=k, v=v, g=g, o=o)
+    chk.add("blocks", blocks, (B, H, nqb, int(blocks.shape[3])), torch.int32, optional=False)
+    chk.add("counts", counts, (B, H, nqb), torch.int32, optional=False).run()
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if o is None:
+            o = torch.empty_like(q)
+        ws, nbytes = _workspace(hla_softmax_anchor_workspace(B, N, H, D), q.device, ws)
+    r = lib().hla_softmax_anchor_block_sparse(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                              float(scale), _ptr(blocks), _ptr(counts), int(blocks.shape[3]),
+                                              _ptr(o), _ptr(ws), nbytes, st.cuda_stream)
+    _check(r, "hla_softmax_anchor_block_sparse")
     return o
 
 
@@ -496,14 +632,30 @@ def hla_attnres_route(sources, w, phi_t=None, eps: float = 1e-6, h=None, alpha=N
     srcs = list(sources)
     if not srcs:
         raise ValueError("need at least one source")
-    B, T, C = (int(x) for x in srcs[0].shape)
+    s0 = srcs[0]
+    if not isinstance(s0, torch.Tensor) or s0.dim() != 3:
+        raise ValueError("sources: expected (B, T, C) tensors")
+    if s0.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"sources: unsupported dtype {s0.dtype}")
+    B, T, C = (int(x) for x in s0.shape)
     S = len(srcs)
-    if h is None:
-        h = torch.empty_like(srcs[0])
-    if alpha is True:
-        alpha = torch.empty((B, T, S), dtype=torch.float32, device=srcs[0].device)
-    arr = (c_void_p * S)(*[_ptr(s) for s in srcs])
-    st = lib().hla_attnres_route(_dtype_code(srcs[0]), B, T, C, S, arr, _ptr(w), _ptr(phi_t), float(eps), _ptr(h),
-                                 _ptr(alpha), _stream(stream))
-    _check(st, "hla_attnres_route")
+    chk = _Checks()
+    for i, src in enumerate(srcs):
+        chk.add(f"sources[{i}]", src, (B, T, C), s0.dtype, optional=False)
+    chk.add("w", w, (C,), torch.float32, optional=False)
+    chk.add("phi_t", phi_t, (B, C), torch.float32)
+    chk.add("h", h, (B, T, C), s0.dtype)
+    if alpha is not True:
+        chk.add("alpha", alpha, (B, T, S), torch.float32)
+    chk.run()
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        if h is None:
+            h = torch.empty_like(s0)
+        if alpha is True:
+            alpha = torch.empty((B, T, S), dtype=torch.float32, device=s0.device)
+    arr = (c_void_p * S)(*[_ptr(x) for x in srcs])
+    r = lib().hla_attnres_route(_dtype_code(s0), B, T, C, S, arr, _ptr(w), _ptr(phi_t), float(eps), _ptr(h),
+                                _ptr(alpha), st.cuda_stream)
+    _check(r, "hla_attnres_route")
     return h, alpha

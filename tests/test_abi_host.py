@@ -309,3 +309,77 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(hla, "_lib", None)
     with pytest.raises(ImportError):
         hla.lib()
+
+
+# ----------------------------------------------------------------------------
+# the Python binding checks every tensor before anything reaches the library
+
+class _NoLibrary:
+    def __getattr__(self, name):
+        raise AssertionError(f"the library was called ({name}) before the argument checks failed")
+
+
+@pytest.fixture
+def no_library(monkeypatch):
+    monkeypatch.setattr(hla, "_lib", _NoLibrary())
+
+
+def _bnhd(*shape, dtype=None):
+    torch = pytest.importorskip("torch")
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", [
+    "k_short", "k_dtype", "g_shape", "o_dtype", "kv_in_shape", "ksum_out_dtype", "anchor_v_shape", "lse_shape",
+    "saved_kv_shape", "grad_do_shape", "route_w_dtype", "route_alpha_shape", "route_source_shape", "rope_grid",
+])
+def test_binding_rejects_mismatched_tensors(no_library, case):
+    torch = pytest.importorskip("torch")
+    B, N, H, D = 1, 12, 2, 64
+    q = _bnhd(B, N, H, D)
+    x = _bnhd(B, N, H, D)
+    f32 = torch.float32
+    with pytest.raises(ValueError) as e:
+        if case == "k_short":
+            hla.hla_linear_attn(q, _bnhd(B, N - 1, H, D), x)
+        elif case == "k_dtype":
+            hla.hla_linear_attn(q, _bnhd(B, N, H, D, dtype=f32), x)
+        elif case == "g_shape":
+            hla.hla_linear_attn(q, x, x, g=_bnhd(B, N, H + 1, D))
+        elif case == "o_dtype":
+            hla.hla_linear_attn(q, x, x, o=_bnhd(B, N, H, D, dtype=f32))
+        elif case == "kv_in_shape":
+            hla.hla_linear_attn_chunked(q, x, x, 4, kv_in=torch.zeros(B, H, D), ksum_in=torch.zeros(B, H, D))
+        elif case == "ksum_out_dtype":
+            hla.hla_linear_attn_chunked(q, x, x, 4, kv_out=torch.zeros(B, H, D, D),
+                                        ksum_out=torch.zeros(B, H, D, dtype=torch.float64))
+        elif case == "anchor_v_shape":
+            hla.hla_softmax_anchor(q, x, _bnhd(B, N + 1, H, D))
+        elif case == "lse_shape":
+            hla.hla_softmax_anchor_lse(q, x, x, lse=torch.zeros(B, N, H))
+        elif case == "saved_kv_shape":
+            hla.hla_linear_attn_backward_saved(q, x, x, torch.zeros(B, H, D), torch.zeros(B, H, D), x)
+        elif case == "grad_do_shape":
+            hla.hla_softmax_anchor_backward(q, x, x, _bnhd(B, N, H, 32))
+        elif case == "route_w_dtype":
+            srcs = [torch.zeros(B, N, 256, dtype=torch.bfloat16) for _ in range(3)]
+            hla.hla_attnres_route(srcs, torch.zeros(256, dtype=torch.bfloat16))
+        elif case == "route_alpha_shape":
+            srcs = [torch.zeros(B, N, 256, dtype=torch.bfloat16) for _ in range(3)]
+            hla.hla_attnres_route(srcs, torch.zeros(256), alpha=torch.zeros(B, N, 4))
+        elif case == "route_source_shape":
+            srcs = [torch.zeros(B, N, 256, dtype=torch.bfloat16) for _ in range(2)] + \
+                   [torch.zeros(B, N - 1, 256, dtype=torch.bfloat16)]
+            hla.hla_attnres_route(srcs, torch.zeros(256))
+        elif case == "rope_grid":
+            tabs = [np.zeros((2, d // 2, 2), np.float32) for d in (16, 24, 24)]
+            r = hla.Rope3D((2, 2, 2), device="cpu", tables=tabs)
+            hla.hla_linear_attn(q, x, x, rope=r)
+    msg = str(e.value)
+    assert "device" not in msg, msg  # the shape or dtype check fires first
+
+
+def test_binding_requires_device_tensors(no_library):
+    q = _bnhd(1, 8, 2, 64)
+    with pytest.raises(ValueError, match="device tensors"):
+        hla.hla_linear_attn(q, q.clone(), q.clone())

@@ -22,13 +22,15 @@ MUTATIONS = [
     ("rope3d.py", "y = (n // Wg) % Hg", "y = (n // Hg) % Wg"),
     ("rope3d.py", "for pos, d in zip((t, y, x), rope.bands)", "for pos, d in zip((t, x, y), rope.bands)"),
     # bidirectional linear attention
-    ("linear_attention.py", 'denominator = np.einsum("bnhd,bhd->bnh", q_relu, k_sum)',
-     'denominator = np.einsum("bnhd,bhd->bnh", q_rope, k_sum)'),
-    ("linear_attention.py", "(denominator[..., None] + eps)", "np.maximum(denominator[..., None], eps)"),
-    ("linear_attention.py", 'kv = np.einsum("bnhd,bnhe->bhde", k_rope, v)', 'kv = np.einsum("bnhd,bnhe->bhed", k_rope, v)'),
-    ("linear_attention.py", "return q_relu, k_relu, rope3d_rotate(q_relu, theta), rope3d_rotate(k_relu, theta)",
-     "return q_relu, k_relu, rope3d_rotate(q_relu, theta), k_relu"),
-    ("linear_attention.py", "out = _sigmoid(g) * out\n    if return_state", "out = (1 - _sigmoid(g)) * out\n    if return_state"),
+    ("linear_attention.py", 'den = np.einsum("id,d->i", phi_q[b, sel, h, :], zsum[b, h]) + eps',
+     'den = np.einsum("id,d->i", rot_q[b, sel, h, :], zsum[b, h]) + eps'),
+    ("linear_attention.py", 'den = np.einsum("id,d->i", phi_q[b, sel, h, :], zsum[b, h]) + eps',
+     'den = np.maximum(np.einsum("id,d->i", phi_q[b, sel, h, :], zsum[b, h]), eps)'),
+    ("linear_attention.py", "state[b, h] = c.T @ v[b, :, h, :]", "state[b, h] = (c.T @ v[b, :, h, :]).T"),
+    ("linear_attention.py", "return pos_q, pos_k, rope3d_rotate(pos_q, theta), rope3d_rotate(pos_k, theta)",
+     "return pos_q, pos_k, rope3d_rotate(pos_q, theta), pos_k"),
+    ("linear_attention.py", "out = _sigmoid(g[:, sel]) * out", "out = (1 - _sigmoid(g[:, sel])) * out"),
+    ("linear_attention.py", "zsum[b, h] = phi_k[b, :, h, :].sum(axis=0)", "zsum[b, h] = phi_q[b, :, h, :].sum(axis=0)"),
     # chunked: exclusive instead of inclusive prefix, dropped key-sum input, wrong key sum, dropped gate
     ("linear_attention.py",
      '        num = np.einsum("bnhd,bhde->bnhe", q_rope[:, start:stop], kv)\n        den',
