@@ -51,6 +51,15 @@
  *   even. Only head dimension D = 64 is built.
  * - Determinism: no floating-point atomics are used; a call repeated on the
  *   same inputs returns bitwise identical outputs.
+ * - Non-finite inputs (a reading; the pages say nothing of them): nothing is
+ *   checked or clamped, and NaN propagates. relu keeps NaN (relu(-Inf) = 0,
+ *   relu(+Inf) = +Inf) and every sum that takes a NaN or Inf term carries it.
+ *   A NaN in q_i reaches o_i only; in k_j every output row of that head (in
+ *   the block-causal forms: the rows of k_j's chunk and of later chunks); in
+ *   v_j[e] column e of the same rows; in g_i[e] that one element; in a router
+ *   source at token t, h_t and alpha_t only. An Inf makes the outputs that
+ *   take it non-finite in the same pattern. Outputs that do not depend on the
+ *   value are unaffected. Gradients of non-finite inputs are unspecified.
  */
 #ifndef HLA_H
 #define HLA_H
@@ -251,8 +260,14 @@ hla_status hla_linear_attn_chunked_backward(hla_dtype dt, int B, int N, int H, i
  * q, k, v, g, o: [B][N][H][D] bf16 (dt must be HLA_BF16); g may be NULL.
  * Products run on bf16 matrix cores with float accumulation and a float
  * online softmax; the probabilities are rounded to bf16 for the P.V product.
+ * The softmax subtracts a per-row reference: the running row maximum, or, for
+ * the rows of a 32-row group whose bound b_i = scale log2(e) |q_i| max_j |k_j|
+ * (Cauchy-Schwarz: no logit exceeds it) is at most 48 in log2 units, b_i itself
+ * (softmax does not depend on the reference; the result differs only in
+ * rounding). Both paths give the same results up to bf16 rounding.
  * ws: device workspace of at least hla_softmax_anchor_workspace(B, N, H, D)
- *     bytes; it receives V transposed per head (contents on entry ignored).
+ *     bytes; it receives V transposed per head and the largest squared K norm
+ *     of every 64-key block (contents on entry ignored).
  * Errors: INVALID_ARG for null q/k/v/o, B, N or H <= 0, scale not finite and
  * positive; UNSUPPORTED for D != 64 or dt != HLA_BF16; WORKSPACE if ws is NULL
  * or ws_bytes is too small.

@@ -29,6 +29,8 @@
 // same reference max, so the result is exact up to rounding.
 #include <string.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace hla {
@@ -38,7 +40,11 @@ namespace {
 constexpr int kBK = 64;            // keys per tile
 constexpr int kKRow = kD + 8;      // bf16 per LDS row of K (144 bytes)
 constexpr int kVRow = kBK + 8;     // bf16 per LDS row of V^T (144 bytes)
+constexpr int kORow = kD + 8;      // bf16 per LDS row of the output stage (144 bytes)
 constexpr float kLazy = 8.0f;      // lazy max threshold, log2 units
+constexpr float kStatic = 48.0f;   // largest static row reference, log2 units
+constexpr int kLateSleep = 4;      // the late wave group's start offset, units of 64 cycles
+constexpr int kVmcnt0 = 0x0F70;    // s_waitcnt immediate: vmcnt(0), other counters free
 constexpr int kWaves = 16;         // waves per work-group, 32 query rows each
 constexpr int kMinWaves = 4;       // waves per SIMD the forward kernel is compiled for
 static_assert(kSparseKBlock == kBK, "a named key block is one tile");
@@ -64,6 +70,10 @@ struct VtArgs {
   const uint16_t *v;
   uint16_t *vt;  // [B*H][64][npad]
   int N, H, npad;
+  // optional: the largest squared norm of the K rows of each 64-key block,
+  // [B*H][npad / 64] (the forward's static row reference)
+  const uint16_t *k;
+  float *kmax2;
 };
 
 __global__ __launch_bounds__(256) void anchor_vt_kernel(VtArgs a) {
@@ -83,6 +93,35 @@ __global__ __launch_bounds__(256) void anchor_vt_kernel(VtArgs a) {
     if (n < a.N) w = load_once_u4(vp + (size_t)n * tok_stride + 8 * dc);
     uint32_t *dst = reinterpret_cast<uint32_t *>(&tile[key][8 * dc]);
     dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
+  }
+  if (a.kmax2) {
+    __shared__ float wmax[4];
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int c = tid + 256 * r;
+      const int key = c >> 3, dc = c & 7;
+      const int n = n0 + key;
+      float ss = 0.f;
+      if (n < a.N) {
+        const uint4 w = load_once_u4(a.k + (vp - a.v) + (size_t)n * tok_stride + 8 * dc);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss += bf16_lo(ws[j]) * bf16_lo(ws[j]) + bf16_hi(ws[j]) * bf16_hi(ws[j]);
+      }
+      // the key's eight chunks sit in eight consecutive lanes
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      ss += __shfl_xor(ss, 4);
+      m = fmaxf(m, ss);
+    }
+    m = fmaxf(m, __shfl_xor(m, 8));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if ((tid & 63) == 0) wmax[tid >> 6] = m;
+    __syncthreads();
+    if (tid == 0)
+      a.kmax2[(size_t)bh * (a.npad / kBK) + blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   }
   __syncthreads();
   uint16_t *out = a.vt + (size_t)bh * kD * a.npad + n0;
@@ -108,6 +147,9 @@ struct FwdArgs {
   uint16_t *o;
   int N, H, npad;
   float c;  // scale * log2(e)
+  // static row reference (nullable): the largest squared K norm of each 64-key
+  // block of the head, [B*H][npad / 64]
+  const float *kmax2;
   // block-sparse form: key tiles named per (b*H + h, query block), [..][max_blocks]
   const int *blocks, *counts;
   int n_qb, max_blocks;
@@ -141,6 +183,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
   constexpr int kLoads = kBK * 8 / kLoaders;
   __shared__ __align__(16) uint16_t ks[2][kBK * kKRow];
   __shared__ __align__(16) uint16_t vs[2][kD * kVRow];
+  // epilogue: each wave's 32 output rows (gate in, o out), whole 128-byte rows
+  __shared__ __align__(16) uint16_t ostage[kPrep ? 1 : WAVES][32 * kORow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -165,9 +209,51 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
       qb[s] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
+  // Q^T resident before the tile loop. Without this wait the loads may still be
+  // pending on the path of the waves that stage no tile, and the compiler then
+  // waits for all loads (the next tile's included) before every tile's first product.
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+
+  // Row reference. By Cauchy-Schwarz every logit of row i obeys
+  // c s_ij <= c |q_i| max_j |k_j| =: b_i, so b_i can stand in for the row max:
+  // softmax does not depend on the reference, and with b_i >= the true max no
+  // weight exceeds 1. The true max is >= -b_i, so while b_i <= kStatic the
+  // row's largest weight is >= 2^(-2 kStatic) and nothing underflows; a wave
+  // whose rows all qualify skips the per-tile row max. Otherwise (or without
+  // the key norms) it keeps the running max.
+  bool stat = false;
+  float mref = -INFINITY, lsum = 0.f;
+  if (a.kmax2) {
+    __shared__ float wk[WAVES];
+    const int nblk = a.npad / kBK;
+    const float *km = a.kmax2 + (size_t)bh * nblk;
+    float m = 0.f;
+    for (int i = tid; i < nblk; i += kThreads) m = fmaxf(m, km[i]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) wk[wave] = m;
+    __syncthreads();
+    m = wk[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) m = fmaxf(m, wk[w]);
+    float qn = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qn += (float)qb[s][j] * (float)qb[s][j];
+    qn += __shfl_xor(qn, 32);
+    const float bnd = a.c * sqrtf(qn) * sqrtf(m);
+    stat = __builtin_amdgcn_readfirstlane(__all(bnd <= kStatic)) != 0;
+    if (stat) mref = bnd;
+  }
+  // Two wave groups per SIMD (bit 2 of the wave index); the second starts each
+  // tile a few hundred cycles late, so the two groups' matrix-core phases fall
+  // less on each other's and more on the other group's vector phase.
+  const bool late = (__builtin_amdgcn_readfirstlane(wave) & 4) != 0;
 
   // tile loader: K (64 keys x 8 chunks) and V^T (64 dims x 8 chunks), 16-byte
-  // chunks spread over the work-group
+  // chunks spread over the work-group; rows past the end of K repeat the last
+  // row (their scores are masked)
   uint4 kreg[kLoads], vreg[kLoads];
   auto load_tile = [&](int t) {
     if (tid >= kLoaders) return;
@@ -176,8 +262,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     for (int r = 0; r < kLoads; ++r) {
       const int c = tid + kLoaders * r;
       const int row = c >> 3, ch = c & 7;
-      const int n = n0 + row;
-      kreg[r] = n < a.N ? *reinterpret_cast<const uint4 *>(kp + (size_t)n * tok_stride + 8 * ch) : make_uint4(0, 0, 0, 0);
+      const int n = min(n0 + row, a.N - 1);
+      kreg[r] = *reinterpret_cast<const uint4 *>(kp + (size_t)n * tok_stride + 8 * ch);
       vreg[r] = *reinterpret_cast<const uint4 *>(vtp + (size_t)row * a.npad + n0 + 8 * ch);
     }
   };
@@ -197,7 +283,6 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[mb][i] = 0.f;
-  float mref = -INFINITY, lsum = 0.f;
 
   const int ntiles = (a.N + kBK - 1) / kBK;
   constexpr int kBlockWaves = kSparseQBlock / 32;
@@ -237,64 +322,92 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
       return (w << 5) + __builtin_ctz(bits);
     }
   };
-  int t = next(0);
-  if (t < ntiles) {
-    load_tile(t);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int buf = 0; t < ntiles; buf ^= 1) {
-    const int tnext = next(t + 1);
-    if (tnext < ntiles) load_tile(tnext);
-    if (kSparse && !((own[t >> 5] >> (t & 31)) & 1u)) {  // not named by this wave's block
-      if (tnext < ntiles) {
-        store_tile(buf ^ 1);
-        __syncthreads();
-      }
-      t = tnext;
-      continue;
+
+  // The tile loop, once with the running max and once with the static
+  // reference: separate copies keep each within the register budget. Both run
+  // the same barriers, so the waves of one work-group may take either.
+  auto tile_loop = [&](auto stat_c) {
+    constexpr bool kStat = decltype(stat_c)::value;
+    int t = next(0);
+    if (t < ntiles) {
+      load_tile(t);
+      store_tile(0);
     }
-
-    // S^T = K Q^T for the 64 keys of this tile; here and in the P.V product the
-    // two accumulators alternate, so each product waits on the other's
-    // predecessor rather than its own
-    f32x16_t sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t kv =
-            *reinterpret_cast<const bf16x8_t *>(&ks[buf][(32 * kb + tl) * kKRow + 16 * s + 8 * half]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qb[s], sacc[kb], 0, 0, 0);
+    __syncthreads();
+    for (int buf = 0; t < ntiles; buf ^= 1) {
+      const int tnext = next(t + 1);
+      if (tnext < ntiles) load_tile(tnext);
+      if (late) __builtin_amdgcn_s_sleep(kLateSleep);
+      if (kSparse && !((own[t >> 5] >> (t & 31)) & 1u)) {  // not named by this wave's block
+        if (tnext < ntiles) {
+          store_tile(buf ^ 1);
+          __syncthreads();
+        }
+        t = tnext;
+        continue;
       }
 
-    // mask keys past the end (last tile only)
-    if ((t + 1) * kBK > a.N) {
+      // S^T = K Q^T for the 64 keys of this tile; here and in the P.V product the
+      // two accumulators alternate, so each product waits on the other's
+      // predecessor rather than its own
+      f32x16_t sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (t * kBK + 32 * kb + 8 * i + 4 * half + j >= a.N) sacc[kb][4 * i + j] = -INFINITY;
-    }
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8_t kv =
+              *reinterpret_cast<const bf16x8_t *>(&ks[buf][(32 * kb + tl) * kKRow + 16 * s + 8 * half]);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qb[s], sacc[kb], 0, 0, 0);
+        }
 
-    // online softmax (exp2 domain); ts is this lane's share of the tile's row sum
-    bf16x8_t pb[2][2];
-    float ts;
-    auto exps = [&](float nm) {
-      ts = 0.f;
+      // mask keys past the end (last tile only)
+      if ((t + 1) * kBK > a.N) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (t * kBK + 32 * kb + 8 * i + 4 * half + j >= a.N) sacc[kb][4 * i + j] = -INFINITY;
+      }
+
+      if constexpr (!kStat) {
+        // running max, refreshed lazily: rows keep their reference until a tile
+        // exceeds it by more than kLazy (log2 units), so weights stay <= 2^kLazy
+        // and the O / row-sum rescale is almost never taken
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        const float mt = max_halves(mx) * a.c;
+        const bool bump = mt > mref + kLazy;
+        if (__any(bump)) {
+          const float mnew = bump ? mt : mref;
+          const float f = exp2f(mref - mnew);
+          mref = mnew;
+          lsum *= f;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[mb][i] *= f;
+        }
+      }
+
+      // weights in the exp2 domain, rounded to bf16 for the P.V product; the row
+      // sum adds the same bf16 weights (two per v_dot2)
+      bf16x8_t pb[2][2];
+      float ts = 0.f;
+      const float nm = -mref;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float p[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], a.c, nm));
-        }
+        for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], a.c, nm));
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const uint4 w = make_uint4(pack_bf16(p[8 * u + 0], p[8 * u + 1]), pack_bf16(p[8 * u + 2], p[8 * u + 3]),
@@ -307,50 +420,31 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
           ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), one, ts, false);
         }
       }
-    };
-    auto row_max = [&]() {
-      float mx = sacc[0][0];
+      lsum += ts;
+
+      // O^T += V^T P^T
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      return max_halves(mx) * a.c;
-    };
-    auto rescale = [&](float mnew) {
-      const float f = exp2f(mref - mnew);
-      mref = mnew;
-      lsum *= f;
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[mb][i] *= f;
-    };
-    {
-      const float mt = row_max();
-      const bool bump = mt > mref + kLazy;
-      if (__any(bump)) rescale(bump ? mt : mref);
-      exps(-mref);
-    }
-    lsum += ts;
+          for (int mb = 0; mb < 2; ++mb) {
+            const bf16x8_t vv =
+                *reinterpret_cast<const bf16x8_t *>(&vs[buf][(32 * mb + tl) * kVRow + 32 * kb + 16 * u + 8 * half]);
+            oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kb][u], oacc[mb], 0, 0, 0);
+          }
 
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8_t vv =
-              *reinterpret_cast<const bf16x8_t *>(&vs[buf][(32 * mb + tl) * kVRow + 32 * kb + 16 * u + 8 * half]);
-          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kb][u], oacc[mb], 0, 0, 0);
-        }
-
-    if (tnext < ntiles) {
-      store_tile(buf ^ 1);  // the other buffer was last read two tiles ago
-      __syncthreads();
+      if (tnext < ntiles) {
+        store_tile(buf ^ 1);  // the other buffer was last read two tiles ago
+        __syncthreads();
+      }
+      t = tnext;
     }
-    t = tnext;
-  }
+  };
+  if (stat)
+    tile_loop(std::true_type{});
+  else
+    tile_loop(std::false_type{});
 
   // normalise, gate, store: lane holds row tl, dims 32*mb + 8*i + 4*half + j
   const int n = q0 + tl;
@@ -398,27 +492,48 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
       }
     }
     return;
-  }
-  if (n < a.N) {
-    if (a.lse_out && half == 0) a.lse_out[(size_t)bh * a.N + n] = (mref + log2f(l)) * 0.6931471805599453f;
-    const size_t row = head_base + (size_t)n * tok_stride;
+  } else {
+    if (n < a.N && a.lse_out && half == 0) a.lse_out[(size_t)bh * a.N + n] = (mref + log2f(l)) * 0.6931471805599453f;
+    // The wave's 32 rows pass through its LDS stage as whole 128-byte rows: the
+    // gate comes in and o goes out one row per eight lanes (16 bytes each), so
+    // every line is read and written whole by one instruction.
+    uint16_t *st = ostage[wave];
+    const int rr = lane >> 3, rc = lane & 7;  // 8 rows per pass, 16-byte chunk rc
+    if (a.g) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int nr = q0 + 8 * p + rr;
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (nr < a.N) w = load_once_u4(a.g + head_base + (size_t)nr * tok_stride + 8 * rc);
+        *reinterpret_cast<uint4 *>(&st[(8 * p + rr) * kORow + 8 * rc]) = w;
+      }
+      wave_lds_fence();
+    }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const size_t off = row + 32 * mb + 8 * i + 4 * half;
+        const int col = 32 * mb + 8 * i + 4 * half;
         float y[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) y[j] = oacc[mb][4 * i + j] * inv;
+        uint2 *sp = reinterpret_cast<uint2 *>(&st[tl * kORow + col]);
         if (a.g) {
-          const uint2 gw = *reinterpret_cast<const uint2 *>(a.g + off);
+          const uint2 gw = *sp;
           y[0] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_lo(gw.x)));
           y[1] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_hi(gw.x)));
           y[2] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_lo(gw.y)));
           y[3] *= __builtin_amdgcn_rcpf(1.f + __expf(-bf16_hi(gw.y)));
         }
-        *reinterpret_cast<uint2 *>(a.o + off) = make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
+        *sp = make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
       }
+    wave_lds_fence();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int nr = q0 + 8 * p + rr;
+      const uint4 w = *reinterpret_cast<const uint4 *>(&st[(8 * p + rr) * kORow + 8 * rc]);
+      if (nr < a.N) *reinterpret_cast<uint4 *>(a.o + head_base + (size_t)nr * tok_stride + 8 * rc) = w;
+    }
   }
 }
 
@@ -781,13 +896,16 @@ __global__ __launch_bounds__(256) void anchor_prep_saved_kernel(PrepArgs a) {
   }
 }
 
-hipError_t launch_vt(const void *x, void *xt, int B, int N, int H, int npad, hipStream_t stream) {
+hipError_t launch_vt(const void *x, void *xt, int B, int N, int H, int npad, hipStream_t stream,
+                     const void *k = nullptr, float *kmax2 = nullptr) {
   VtArgs va;
   va.v = reinterpret_cast<const uint16_t *>(x);
   va.vt = reinterpret_cast<uint16_t *>(xt);
   va.N = N;
   va.H = H;
   va.npad = npad;
+  va.k = reinterpret_cast<const uint16_t *>(k);
+  va.kmax2 = kmax2;
   hipLaunchKernelGGL(anchor_vt_kernel, dim3(npad / kBK, B * H), dim3(256), 0, stream, va);
   return hipGetLastError();
 }
@@ -796,9 +914,9 @@ hipError_t launch_vt(const void *x, void *xt, int B, int N, int H, int npad, hip
 
 namespace {
 // gradient workspace: V^T, Q^T, dY^T, K^T (bf16, [B*H][64][npad]), dY (bf16, the
-// layout of q), L and Delta (fp32, [B*H][N])
+// layout of q), L and Delta (fp32, [B*H][N]), the key-block norms of the preparation forward
 struct BwdLayout {
-  size_t vt, qt, dyt, kt, dy, lse, delta, total;
+  size_t vt, qt, dyt, kt, dy, lse, delta, kmax2, total;
 };
 BwdLayout bwd_layout(int B, int N, int H) {
   const size_t npad = ((size_t)N + kBK - 1) / kBK * kBK;
@@ -811,7 +929,8 @@ BwdLayout bwd_layout(int B, int N, int H) {
   l.dy = 4 * t;
   l.lse = l.dy + align256((size_t)B * N * H * kD * sizeof(uint16_t));
   l.delta = l.lse + align256((size_t)B * H * N * sizeof(float));
-  l.total = l.delta + align256((size_t)B * H * N * sizeof(float));
+  l.kmax2 = l.delta + align256((size_t)B * H * N * sizeof(float));
+  l.total = l.kmax2 + align256((size_t)B * H * (npad / kBK) * sizeof(float));
   return l;
 }
 }  // namespace
@@ -849,7 +968,9 @@ hipError_t launch_anchor_backward(const AnchorBwdArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(anchor_prep_saved_kernel, dim3((unsigned)((pa.rows + 31) / 32)), dim3(256), 0, stream, pa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
-    if ((e = launch_vt(a.v, vt, a.B, a.N, a.H, npad, stream)) != hipSuccess) return e;
+    float *kmax2 = reinterpret_cast<float *>(ws + l.kmax2);
+    if ((e = launch_vt(a.v, vt, a.B, a.N, a.H, npad, stream, a.k, kmax2)) != hipSuccess) return e;
+    fa.kmax2 = kmax2;
     // preparation: the forward with its epilogue writing dG, dY, L, Delta
     fa.q = reinterpret_cast<const uint16_t *>(a.q);
     fa.k = reinterpret_cast<const uint16_t *>(a.k);
@@ -906,15 +1027,19 @@ size_t anchor_sparse_lds_bytes(int N) {
   return nwords * (1 + kWaves / (kSparseQBlock / 32)) * sizeof(uint32_t);
 }
 
+// forward workspace: V^T (bf16, [B*H][64][npad]), then the key-block norms
+// (fp32, [B*H][npad / 64])
 size_t anchor_workspace_bytes(int B, int N, int H) {
   const size_t npad = ((size_t)N + kBK - 1) / kBK * kBK;
-  return (size_t)B * H * kD * npad * sizeof(uint16_t);
+  return align256((size_t)B * H * kD * npad * sizeof(uint16_t)) + (size_t)B * H * (npad / kBK) * sizeof(float);
 }
 
 hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   const int heads = a.B * a.H;
   const int npad = (a.N + kBK - 1) / kBK * kBK;
-  hipError_t e = launch_vt(a.v, a.ws, a.B, a.N, a.H, npad, stream);
+  float *kmax2 = reinterpret_cast<float *>(reinterpret_cast<char *>(a.ws) +
+                                           align256((size_t)heads * kD * npad * sizeof(uint16_t)));
+  hipError_t e = launch_vt(a.v, a.ws, a.B, a.N, a.H, npad, stream, a.k, kmax2);
   if (e != hipSuccess) return e;
 
   FwdArgs fa;
@@ -932,6 +1057,7 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   fa.counts = a.counts;
   fa.max_blocks = a.max_blocks;
   fa.lse_out = a.lse;
+  fa.kmax2 = kmax2;
   if (a.blocks) {
     fa.n_qb = (a.N + kSparseQBlock - 1) / kSparseQBlock;
     hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, true, false>),

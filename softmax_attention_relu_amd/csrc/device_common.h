@@ -20,6 +20,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// The feature map phi(x) = max(x, 0) with NaN kept (IEEE 754-2019 maximum,
+// one v_maximum3_f32): a NaN input reaches every output that depends on it,
+// where the maxNum of fmaxf would turn it into 0.
+__device__ __forceinline__ float relu(float x) { return __builtin_elementwise_maximum(x, 0.0f); }
+
 // Round two floats to bf16 (nearest even, v_cvt_pk_bf16_f32) and pack them.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   f32x2_t x = {a, b};

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256, kBF16 ? 2 : 1) void la_build_kernel(BuildArgs 
       E::unpack(kr[r], x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        x[i] = fmaxf(x[i], 0.f);
+        x[i] = relu(x[i]);
         if constexpr (kZW)
           zacc[i] += zw[r] * x[i];
         else
@@ -686,7 +686,7 @@ __global__ __launch_bounds__(256, kRopeMode == kRopePair ? 1 : 2) void la_apply_
       x[6] = bf16_lo(qr[s].w); x[7] = bf16_hi(qr[s].w);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        x[t] = fmaxf(x[t], 0.f);
+        x[t] = relu(x[t]);
         den += x[t] * zr[s][t];
       }
       if constexpr (kRope) {
@@ -795,7 +795,7 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
     float den = 0.f;
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
-      x[s] = fmaxf(x[s], 0.f);
+      x[s] = relu(x[s]);
       den += x[s] * zr[s];
     }
     if (a.rope.enabled) {
@@ -1043,10 +1043,10 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
       const uint32_t kw[4] = {k0.x, k0.y, k1.x, k1.y};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        fq[2 * u] = fmaxf(bf16_lo(qw[u]), 0.f);
-        fq[2 * u + 1] = fmaxf(bf16_hi(qw[u]), 0.f);
-        fk[2 * u] = fmaxf(bf16_lo(kw[u]), 0.f);
-        fk[2 * u + 1] = fmaxf(bf16_hi(kw[u]), 0.f);
+        fq[2 * u] = relu(bf16_lo(qw[u]));
+        fq[2 * u + 1] = relu(bf16_hi(qw[u]));
+        fk[2 * u] = relu(bf16_lo(kw[u]));
+        fk[2 * u + 1] = relu(bf16_hi(kw[u]));
       }
       // denominator against the key sum before this step
       {

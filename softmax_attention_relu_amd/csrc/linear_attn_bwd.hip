@@ -209,7 +209,7 @@ __device__ __forceinline__ u32x4_t features(const u32x4_t w, const f32x2_t cs[4]
   unpack8(w, x);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    x[t] = fmaxf(x[t], 0.f);
+    x[t] = relu(x[t]);
     if (z) dot += x[t] * z[t];
   }
   if constexpr (kRope) {

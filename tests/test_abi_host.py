@@ -79,7 +79,8 @@ def test_workspace_sizes(L):
     # one chunk covering everything needs the same as the bidirectional call
     assert hla.hla_linear_attn_chunked_workspace(2, 999, 3, 64, 999) == hla.hla_linear_attn_workspace(2, 999, 3, 64)
     wa = hla.hla_softmax_anchor_workspace(1, 75600, 32, 64)
-    assert wa == 32 * 64 * 75648 * 2  # V^T padded to 64 tokens
+    vt = 32 * 64 * 75648 * 2  # V^T padded to 64 tokens
+    assert wa == -(-vt // 256) * 256 + 32 * (75648 // 64) * 4  # then one K norm per 64-key block
 
 
 def _rope(grid=(2, 2, 2), bands=(16, 24, 24)):
