@@ -134,6 +134,25 @@ hla_status hla_linear_attn(hla_dtype dt, int B, int N, int H, int D,
                            void *o, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * hla_linear_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The workspace is the library's own static
+ * device array of hla_linear_attn_noalloc_max_workspace() bytes (64 MiB), one
+ * per GPU, held until the process ends; the call allocates nothing and
+ * returns results bitwise equal to hla_linear_attn's. Every call on one GPU
+ * uses that GPU's array, so calls that overlap on one GPU (several streams or
+ * host threads) race; serialise them. The caller passes inputs and outputs as
+ * for hla_linear_attn; the current device must be the one that owns them.
+ * Errors: as hla_linear_attn; WORKSPACE when the call needs more than the
+ * static array (hla_linear_attn_workspace(B, N, H, D) above the maximum), HIP
+ * when the array's address cannot be obtained on the current device.
+ */
+size_t hla_linear_attn_noalloc_max_workspace(void);
+hla_status hla_linear_attn_noalloc(hla_dtype dt, int B, int N, int H, int D,
+                                   const void *q, const void *k, const void *v, const void *g,
+                                   const hla_rope3d *rope, float eps, void *o, hipStream_t stream);
+
+/*
  * Block-causal linear attention with a constant-memory carried state
  * (SANA-Video notes, section 3.4: causal equation with the own term included,
  * the cache of cumulative states and key sums, and Algorithm 1's update).

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "hla_internal.h"
 
 using namespace hla;
@@ -159,6 +161,55 @@ hla_status hla_linear_attn(hla_dtype dt, int B, int N, int H, int D, const void 
                            hipStream_t stream) {
   return linear_common(dt, B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, nullptr, nullptr, o,
                        ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free bidirectional call: the workspace is the library's own
+// static device array. Each GPU the library runs on holds one copy until the
+// process ends; its address on a device comes from hipGetSymbolAddress with that
+// device current, taken on the first call there and kept. In host code the
+// array's name is only a stand-in, so kernels get the kept address.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_on[kMaxDevices];
+
+hla_status scratch_ptr(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HLA_ERR_HIP;
+  void *p = scratch_on[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // idempotent: concurrent first calls on one device store the same address
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HLA_ERR_HIP;
+    scratch_on[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return HLA_OK;
+}
+}  // namespace
+
+size_t hla_linear_attn_noalloc_max_workspace(void) { return kScratchBytes; }
+
+hla_status hla_linear_attn_noalloc(hla_dtype dt, int B, int N, int H, int D, const void *q, const void *k,
+                                   const void *v, const void *g, const hla_rope3d *rope, float eps, void *o,
+                                   hipStream_t stream) {
+  // the same checks as hla_linear_attn, then the size limit, before the scratch
+  // address is looked up (no device call for a rejected request)
+  if (!q || !k || !v || !o) return HLA_ERR_INVALID_ARG;
+  if (!shape_ok(B, N, H)) return HLA_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || isinf(eps)) return HLA_ERR_INVALID_ARG;
+  if (dt != HLA_BF16 && dt != HLA_F32) return HLA_ERR_UNSUPPORTED;
+  if (D != kD) return HLA_ERR_UNSUPPORTED;
+  if (!rope_valid(rope, N, D)) return HLA_ERR_INVALID_ARG;
+  if (plan_linear(B, N, H, N).total_bytes > kScratchBytes) return HLA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const hla_status st = scratch_ptr(&ws);
+  if (st != HLA_OK) return st;
+  // every byte of the workspace that the kernels read they first write (the
+  // slab partials, then the prefix records), so nothing needs clearing
+  return linear_common(dt, B, N, H, D, N, q, k, v, g, rope, eps, nullptr, nullptr, nullptr, nullptr, o, ws,
+                       kScratchBytes, stream);
 }
 
 size_t hla_linear_attn_chunked_workspace(int B, int N, int H, int D, int chunk_tokens) {

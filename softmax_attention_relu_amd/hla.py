@@ -27,6 +27,8 @@ EXPORTS = (
     "hla_rope_table_host",
     "hla_linear_attn_workspace",
     "hla_linear_attn",
+    "hla_linear_attn_noalloc_max_workspace",
+    "hla_linear_attn_noalloc",
     "hla_linear_attn_chunked_workspace",
     "hla_linear_attn_chunked",
     "hla_linear_attn_causal_workspace",
@@ -79,6 +81,11 @@ def lib() -> ctypes.CDLL:
         L.hla_linear_attn.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                       POINTER(hla_rope3d), c_float, c_void_p, c_void_p, c_size_t, c_void_p]
         L.hla_linear_attn.restype = c_int
+        L.hla_linear_attn_noalloc_max_workspace.argtypes = []
+        L.hla_linear_attn_noalloc_max_workspace.restype = c_size_t
+        L.hla_linear_attn_noalloc.argtypes = [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, POINTER(hla_rope3d), c_float, c_void_p, c_void_p]
+        L.hla_linear_attn_noalloc.restype = c_int
         L.hla_linear_attn_chunked_workspace.argtypes = [c_int, c_int, c_int, c_int, c_int]
         L.hla_linear_attn_chunked_workspace.restype = c_size_t
         L.hla_linear_attn_chunked.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
@@ -357,6 +364,31 @@ def hla_linear_attn(q, k, v, g=None, rope: Rope3D | None = None, eps: float = 1e
     r = lib().hla_linear_attn(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _rope_ptr(rope),
                               float(eps), _ptr(o), _ptr(ws), nbytes, st.cuda_stream)
     _check(r, "hla_linear_attn")
+    return o
+
+
+def hla_linear_attn_noalloc_max_workspace() -> int:
+    return int(lib().hla_linear_attn_noalloc_max_workspace())
+
+
+def hla_linear_attn_noalloc(q, k, v, g=None, rope: Rope3D | None = None, eps: float = 1e-6, o=None, stream=None):
+    """hla_linear_attn with the library's static workspace (the C call allocates nothing); returns o.
+
+    Calls that overlap on one GPU share that workspace and race. ``o`` is allocated here when not given.
+    """
+    torch = _torch()
+    B, N, H, D = _bnhd(q)
+    chk = _like(_Checks(), q, q=q, k=k, v=v, g=g, o=o)
+    _check_rope(rope, N, D)
+    chk.run()
+    _check_rope(rope, N, D, q.device)
+    st = _stream_obj(stream)
+    if o is None:
+        with torch.cuda.stream(st):
+            o = torch.empty_like(q)
+    r = lib().hla_linear_attn_noalloc(_dtype_code(q), B, N, H, D, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                      _rope_ptr(rope), float(eps), _ptr(o), st.cuda_stream)
+    _check(r, "hla_linear_attn_noalloc")
     return o
 
 

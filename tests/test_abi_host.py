@@ -32,10 +32,23 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     assert sorted(hla.EXPORTS) == names
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_noalloc_validation(L):
+    assert hla.hla_linear_attn_noalloc_max_workspace() == 64 << 20
+    rope = _rope()
+    call = L.hla_linear_attn_noalloc
+    assert call(0, 1, 8, 1, 64, None, FAKE, FAKE, None, None, 1e-6, FAKE, None) == hla.HLA_ERR_INVALID_ARG
+    assert call(0, 1, 8, 1, 32, FAKE, FAKE, FAKE, None, None, 1e-6, FAKE, None) == hla.HLA_ERR_UNSUPPORTED
+    assert call(0, 1, 9, 1, 64, FAKE, FAKE, FAKE, None, ctypes.byref(rope), 1e-6, FAKE, None) == \
+        hla.HLA_ERR_INVALID_ARG
+    # partial sums above the static array: rejected before any device call
+    assert hla.hla_linear_attn_workspace(64, 4096, 64, 64) > 64 << 20
+    assert call(0, 64, 4096, 64, 64, FAKE, FAKE, FAKE, None, None, 1e-6, FAKE, None) == hla.HLA_ERR_WORKSPACE
 
 
 def test_status_strings(L):
