@@ -1249,21 +1249,38 @@ LinearPlan plan_linear(int B, int N, int H, int chunk_tokens) {
   p.n_chunks = (int)((N + L - 1) / L);
   p.ngroups = (H + kHeadsPerWG - 1) / kHeadsPerWG;
   // Work-groups per (b, head group, chunk). Both kernels run two work-groups
-  // per CU, 512 at once on 256 CUs. A last round that is only partly filled
-  // leaves bandwidth unused (600 work-groups ran 30% slower than 1000 on the
-  // 720p/60s shape), so the split is the one, up to four rounds, whose
-  // work-groups fill their rounds best; the smaller split wins a tie. A chunk
-  // never gets more slabs than 64-token tiles, nor more parts than 32-token steps.
+  // per CU, 512 at once on the 256 CUs of an MI355X (a fixed assumption, so
+  // that the workspace query needs no device). Work-groups start in grid order
+  // as slots free up. The split chosen is the one, up to four rounds of
+  // work-groups, whose schedule ends first, estimated from each work-group's
+  // 64-token tiles plus one tile's worth of start-up: the work-groups of full
+  // chunks run in rounds, and those of a shorter last chunk fill the slots the
+  // last round leaves idle. The smaller split wins a tie. A chunk never gets
+  // more slabs than tiles, nor more parts than 32-token steps.
   const long long per_chunk_groups = (long long)B * p.ngroups * p.n_chunks;
   const long long slots = 512;
   const long long max_split = std::max(1LL, 4 * slots / per_chunk_groups);
-  long long split = 1;
-  double best_fill = -1.0;
-  for (long long sp = 1; sp <= max_split; ++sp) {
-    const long long wgs = sp * per_chunk_groups;
-    const double fill = (double)wgs / (double)(slots * ((wgs + slots - 1) / slots));
-    if (fill > best_fill + 1e-9) {
-      best_fill = fill;
+  const long long tiles_full = (L + kWTile - 1) / kWTile;
+  const long long last_len = N - (long long)(p.n_chunks - 1) * L;
+  const long long tiles_last = (last_len + kWTile - 1) / kWTile;
+  const bool ragged = tiles_last < tiles_full;
+  long long split = 1, best_end = -1;
+  for (long long sp = 1; sp <= std::min(max_split, tiles_full); ++sp) {
+    const long long groups = (long long)B * p.ngroups;
+    const long long n_full = groups * (p.n_chunks - (ragged ? 1 : 0)) * sp;
+    const long long n_last = ragged ? groups * sp : 0;
+    const long long d_full = 1 + (tiles_full + sp - 1) / sp;
+    const long long d_last = 1 + (tiles_last + sp - 1) / sp;
+    const long long rounds = (n_full + slots - 1) / slots;
+    const long long idle = rounds * slots - n_full;  // slots free after rounds - 1
+    long long end = rounds * d_full;
+    if (n_last > 0) {
+      const long long small_end = idle > 0 ? (rounds - 1) * d_full + (n_last + idle - 1) / idle * d_last
+                                           : rounds * d_full + (n_last + slots - 1) / slots * d_last;
+      end = std::max(end, small_end);
+    }
+    if (best_end < 0 || end < best_end) {
+      best_end = end;
       split = sp;
     }
   }
