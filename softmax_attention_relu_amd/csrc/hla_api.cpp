@@ -14,6 +14,17 @@ static_assert(kSparseQBlock == HLA_SPARSE_Q_BLOCK && kSparseKBlock == HLA_SPARSE
 
 namespace {
 
+// Enum arguments come from C, where any int value can be passed. Their bits are
+// read as an int before they are validated: loading a value outside the enum's
+// range as the C++ enum type is undefined behaviour.
+template <class E>
+int enum_bits(const E *e) {
+  static_assert(sizeof(E) == sizeof(int), "the interface's enums are int-sized");
+  int v;
+  memcpy(&v, e, sizeof v);
+  return v;
+}
+
 bool rope_valid(const hla_rope3d *r, int N, int D) {
   if (!r) return true;
   if (r->grid_t <= 0 || r->grid_h <= 0 || r->grid_w <= 0) return false;
@@ -54,7 +65,7 @@ bool shape_ok(int B, int N, int H) {
   return true;
 }
 
-hla_status linear_common(hla_dtype dt, int B, int N, int H, int D, int chunk_tokens, const void *q, const void *k,
+hla_status linear_common(int dtv, int B, int N, int H, int D, int chunk_tokens, const void *q, const void *k,
                          const void *v, const void *g, const hla_rope3d *rope, float eps, const float *kv_in,
                          const float *ksum_in, float *kv_out, float *ksum_out, void *o, void *ws, size_t ws_bytes,
                          hipStream_t stream) {
@@ -63,7 +74,7 @@ hla_status linear_common(hla_dtype dt, int B, int N, int H, int D, int chunk_tok
   if ((kv_in == nullptr) != (ksum_in == nullptr)) return HLA_ERR_INVALID_ARG;
   if ((kv_out == nullptr) != (ksum_out == nullptr)) return HLA_ERR_INVALID_ARG;
   if (!(eps >= 0.f) || isinf(eps)) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 && dt != HLA_F32) return HLA_ERR_UNSUPPORTED;
+  if (dtv != HLA_BF16 && dtv != HLA_F32) return HLA_ERR_UNSUPPORTED;
   if (D != kD) return HLA_ERR_UNSUPPORTED;
   if (!rope_valid(rope, N, D)) return HLA_ERR_INVALID_ARG;
   const LinearPlan plan = plan_linear(B, N, H, chunk_tokens);
@@ -84,10 +95,10 @@ hla_status linear_common(hla_dtype dt, int B, int N, int H, int D, int chunk_tok
   a.kv_out = kv_out;
   a.ksum_out = ksum_out;
   a.ws = ws;
-  return launch_linear(dt, a, plan, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
+  return launch_linear(static_cast<hla_dtype>(dtv), a, plan, stream) == hipSuccess ? HLA_OK : HLA_ERR_HIP;
 }
 
-hla_status linear_bwd_common(hla_dtype dt, int B, int N, int H, int D, int chunk_tokens, const void *q,
+hla_status linear_bwd_common(int dtv, int B, int N, int H, int D, int chunk_tokens, const void *q,
                              const void *k, const void *v, const void *g, const hla_rope3d *rope, float eps,
                              const float *kv_in, const float *ksum_in, const void *dO, const float *dkv_out,
                              const float *dksum_out, void *dq, void *dk, void *dv, void *dg, float *dkv_in,
@@ -100,10 +111,10 @@ hla_status linear_bwd_common(hla_dtype dt, int B, int N, int H, int D, int chunk
   if ((dkv_out == nullptr) != (dksum_out == nullptr)) return HLA_ERR_INVALID_ARG;
   if ((dkv_in == nullptr) != (dksum_in == nullptr)) return HLA_ERR_INVALID_ARG;
   if (!(eps >= 0.f) || isinf(eps)) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 && dt != HLA_F32) return HLA_ERR_UNSUPPORTED;
+  if (dtv != HLA_BF16 && dtv != HLA_F32) return HLA_ERR_UNSUPPORTED;
   if (D != kD) return HLA_ERR_UNSUPPORTED;
   if (!rope_valid(rope, N, D)) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16) return HLA_ERR_UNSUPPORTED;
+  if (dtv != HLA_BF16) return HLA_ERR_UNSUPPORTED;
   const LinearPlan plan = plan_linear_backward(B, N, H, chunk_tokens);
   if (!ws || ws_bytes < plan.total_bytes) return HLA_ERR_WORKSPACE;
   LinearBwdArgs a;
@@ -159,7 +170,7 @@ size_t hla_linear_attn_workspace(int B, int N, int H, int D) {
 hla_status hla_linear_attn(hla_dtype dt, int B, int N, int H, int D, const void *q, const void *k, const void *v,
                            const void *g, const hla_rope3d *rope, float eps, void *o, void *ws, size_t ws_bytes,
                            hipStream_t stream) {
-  return linear_common(dt, B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, nullptr, nullptr, o,
+  return linear_common(enum_bits(&dt), B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, nullptr, nullptr, o,
                        ws, ws_bytes, stream);
 }
 
@@ -199,7 +210,7 @@ hla_status hla_linear_attn_noalloc(hla_dtype dt, int B, int N, int H, int D, con
   if (!q || !k || !v || !o) return HLA_ERR_INVALID_ARG;
   if (!shape_ok(B, N, H)) return HLA_ERR_INVALID_ARG;
   if (!(eps >= 0.f) || isinf(eps)) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 && dt != HLA_F32) return HLA_ERR_UNSUPPORTED;
+  if (enum_bits(&dt) != HLA_BF16 && enum_bits(&dt) != HLA_F32) return HLA_ERR_UNSUPPORTED;
   if (D != kD) return HLA_ERR_UNSUPPORTED;
   if (!rope_valid(rope, N, D)) return HLA_ERR_INVALID_ARG;
   if (plan_linear(B, N, H, N).total_bytes > kScratchBytes) return HLA_ERR_WORKSPACE;
@@ -208,7 +219,7 @@ hla_status hla_linear_attn_noalloc(hla_dtype dt, int B, int N, int H, int D, con
   if (st != HLA_OK) return st;
   // every byte of the workspace that the kernels read they first write (the
   // slab partials, then the prefix records), so nothing needs clearing
-  return linear_common(dt, B, N, H, D, N, q, k, v, g, rope, eps, nullptr, nullptr, nullptr, nullptr, o, ws,
+  return linear_common(enum_bits(&dt), B, N, H, D, N, q, k, v, g, rope, eps, nullptr, nullptr, nullptr, nullptr, o, ws,
                        kScratchBytes, stream);
 }
 
@@ -221,7 +232,7 @@ hla_status hla_linear_attn_chunked(hla_dtype dt, int B, int N, int H, int D, int
                                    const void *k, const void *v, const void *g, const hla_rope3d *rope, float eps,
                                    const float *kv_in, const float *ksum_in, float *kv_out, float *ksum_out, void *o,
                                    void *ws, size_t ws_bytes, hipStream_t stream) {
-  return linear_common(dt, B, N, H, D, chunk_tokens, q, k, v, g, rope, eps, kv_in, ksum_in, kv_out, ksum_out, o, ws,
+  return linear_common(enum_bits(&dt), B, N, H, D, chunk_tokens, q, k, v, g, rope, eps, kv_in, ksum_in, kv_out, ksum_out, o, ws,
                        ws_bytes, stream);
 }
 
@@ -239,10 +250,10 @@ hla_status hla_linear_attn_causal(hla_dtype dt, int B, int N, int H, int D, cons
   if ((kv_in == nullptr) != (ksum_in == nullptr)) return HLA_ERR_INVALID_ARG;
   if ((kv_out == nullptr) != (ksum_out == nullptr)) return HLA_ERR_INVALID_ARG;
   if (!(eps >= 0.f) || isinf(eps)) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 && dt != HLA_F32) return HLA_ERR_UNSUPPORTED;
+  if (enum_bits(&dt) != HLA_BF16 && enum_bits(&dt) != HLA_F32) return HLA_ERR_UNSUPPORTED;
   if (D != kD) return HLA_ERR_UNSUPPORTED;
   if (!rope_valid(rope, N, D)) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16) return HLA_ERR_UNSUPPORTED;
+  if (enum_bits(&dt) != HLA_BF16) return HLA_ERR_UNSUPPORTED;
   LinearArgs a;
   a.B = B;
   a.N = N;
@@ -274,7 +285,7 @@ hla_status hla_linear_attn_backward(hla_dtype dt, int B, int N, int H, int D, co
                                     const void *v, const void *g, const hla_rope3d *rope, float eps, const void *dO,
                                     void *dq, void *dk, void *dv, void *dg, void *ws, size_t ws_bytes,
                                     hipStream_t stream) {
-  return linear_bwd_common(dt, B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, dO, nullptr,
+  return linear_bwd_common(enum_bits(&dt), B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, dO, nullptr,
                            nullptr, dq, dk, dv, dg, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
@@ -283,7 +294,7 @@ hla_status hla_linear_attn_backward_saved(hla_dtype dt, int B, int N, int H, int
                                           const float *kv, const float *ksum, const void *dO, void *dq, void *dk,
                                           void *dv, void *dg, void *ws, size_t ws_bytes, hipStream_t stream) {
   if (!kv || !ksum) return HLA_ERR_INVALID_ARG;
-  return linear_bwd_common(dt, B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, dO, nullptr,
+  return linear_bwd_common(enum_bits(&dt), B, N, H, D, N > 0 ? N : 1, q, k, v, g, rope, eps, nullptr, nullptr, dO, nullptr,
                            nullptr, dq, dk, dv, dg, nullptr, nullptr, ws, ws_bytes, stream, kv, ksum);
 }
 
@@ -299,7 +310,7 @@ hla_status hla_linear_attn_chunked_backward(hla_dtype dt, int B, int N, int H, i
                                             const float *dksum_out, void *dq, void *dk, void *dv, void *dg,
                                             float *dkv_in, float *dksum_in, void *ws, size_t ws_bytes,
                                             hipStream_t stream) {
-  return linear_bwd_common(dt, B, N, H, D, chunk_tokens, q, k, v, g, rope, eps, kv_in, ksum_in, dO, dkv_out,
+  return linear_bwd_common(enum_bits(&dt), B, N, H, D, chunk_tokens, q, k, v, g, rope, eps, kv_in, ksum_in, dO, dkv_out,
                            dksum_out, dq, dk, dv, dg, dkv_in, dksum_in, ws, ws_bytes, stream);
 }
 
@@ -312,7 +323,7 @@ hla_status hla_softmax_anchor(hla_dtype dt, int B, int N, int H, int D, const vo
                               const void *g, float scale, void *o, void *ws, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !o) return HLA_ERR_INVALID_ARG;
   if (!shape_ok(B, N, H) || !isfinite(scale) || !(scale > 0.f)) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
+  if (enum_bits(&dt) != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < anchor_workspace_bytes(B, N, H)) return HLA_ERR_WORKSPACE;
   AnchorArgs a;
   a.B = B;
@@ -334,7 +345,7 @@ hla_status hla_softmax_anchor_lse(hla_dtype dt, int B, int N, int H, int D, cons
   if (!lse) return HLA_ERR_INVALID_ARG;
   if (!q || !k || !v || !o) return HLA_ERR_INVALID_ARG;
   if (!shape_ok(B, N, H) || !isfinite(scale) || !(scale > 0.f)) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
+  if (enum_bits(&dt) != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < anchor_workspace_bytes(B, N, H)) return HLA_ERR_WORKSPACE;
   AnchorArgs a;
   a.B = B;
@@ -363,7 +374,7 @@ hla_status hla_softmax_anchor_backward(hla_dtype dt, int B, int N, int H, int D,
   if (!q || !k || !v || !dO || !dq || !dk || !dv) return HLA_ERR_INVALID_ARG;
   if ((g == nullptr) != (dg == nullptr)) return HLA_ERR_INVALID_ARG;
   if (!shape_ok(B, N, H) || !isfinite(scale) || !(scale > 0.f)) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
+  if (enum_bits(&dt) != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < anchor_backward_workspace_bytes(B, N, H)) return HLA_ERR_WORKSPACE;
   AnchorBwdArgs a;
   a.B = B;
@@ -391,7 +402,7 @@ hla_status hla_softmax_anchor_backward_saved(hla_dtype dt, int B, int N, int H, 
   if (!q || !k || !v || !dO || !dq || !dk || !dv) return HLA_ERR_INVALID_ARG;
   if ((g == nullptr) != (dg == nullptr)) return HLA_ERR_INVALID_ARG;
   if (!shape_ok(B, N, H) || !isfinite(scale) || !(scale > 0.f)) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
+  if (enum_bits(&dt) != HLA_BF16 || D != kD) return HLA_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < anchor_backward_workspace_bytes(B, N, H)) return HLA_ERR_WORKSPACE;
   AnchorBwdArgs a;
   a.B = B;
@@ -419,7 +430,7 @@ hla_status hla_softmax_anchor_block_sparse(hla_dtype dt, int B, int N, int H, in
                                            hipStream_t stream) {
   if (!q || !k || !v || !o || !blocks || !counts) return HLA_ERR_INVALID_ARG;
   if (!shape_ok(B, N, H) || !isfinite(scale) || !(scale > 0.f) || max_blocks <= 0) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 || D != kD || anchor_sparse_lds_bytes(N) > kSparseLdsLimit) return HLA_ERR_UNSUPPORTED;
+  if (enum_bits(&dt) != HLA_BF16 || D != kD || anchor_sparse_lds_bytes(N) > kSparseLdsLimit) return HLA_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < anchor_workspace_bytes(B, N, H)) return HLA_ERR_WORKSPACE;
   AnchorArgs a;
   a.B = B;
@@ -446,7 +457,7 @@ hla_status hla_attnres_route(hla_dtype dt, int B, int T, int C, int S, const voi
   if (!(eps >= 0.f) || isinf(eps)) return HLA_ERR_INVALID_ARG;
   for (int i = 0; i < S; ++i)
     if (!v[i]) return HLA_ERR_INVALID_ARG;
-  if (dt != HLA_BF16 && dt != HLA_F32) return HLA_ERR_UNSUPPORTED;
+  if (enum_bits(&dt) != HLA_BF16 && enum_bits(&dt) != HLA_F32) return HLA_ERR_UNSUPPORTED;
   if (C > 4096) return HLA_ERR_UNSUPPORTED;
   RouteArgs a;
   memset(&a, 0, sizeof(a));
@@ -464,7 +475,7 @@ hla_status hla_attnres_route(hla_dtype dt, int B, int T, int C, int S, const voi
 }
 
 const char *hla_status_string(hla_status s) {
-  switch (s) {
+  switch (enum_bits(&s)) {
     case HLA_OK: return "HLA_OK";
     case HLA_ERR_INVALID_ARG: return "HLA_ERR_INVALID_ARG: invalid argument";
     case HLA_ERR_UNSUPPORTED: return "HLA_ERR_UNSUPPORTED: unsupported dtype or head dimension";

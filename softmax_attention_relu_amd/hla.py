@@ -17,7 +17,8 @@ from ctypes import POINTER, c_double, c_float, c_int, c_size_t, c_void_p
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhla.so")
+# HLA_LIBRARY selects another build of the library (e.g. the host-sanitizer build)
+LIB_PATH = os.environ.get("HLA_LIBRARY") or os.path.join(_PKG, "libhla.so")
 
 HLA_OK, HLA_ERR_INVALID_ARG, HLA_ERR_UNSUPPORTED, HLA_ERR_WORKSPACE, HLA_ERR_HIP = range(5)
 HLA_BF16, HLA_F32 = 0, 1
