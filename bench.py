@@ -12,7 +12,7 @@ the 720p/5s shape (tokens per second of one layer, B*N / median layer time);
 ``ms_per_step`` is the wall time of a whole group. Per-call times are the
 median (and min) over the timed steps, from HIP events recorded on the stream
 the library launches on. ``legs`` adds, each as the median and min of repeated
-calls with a 1 GiB write before every call (outside the timed region): the
+calls with a 1 GiB read before every call (outside the timed region): the
 cond/uncond pair (B=2, N=32760), the token-causal and the backward passes at
 720p/5s, the block-sparse anchor, the block-causal 720p/60s call (N=867600,
 chunks of 36000), the same sequence streamed block by block for a cond/uncond
@@ -244,11 +244,12 @@ def main() -> int:
     prof = args.profile_leg
     run_legs = not args.no_legs
 
-    # 1 GiB written between timed iterations (outside the timed region) evicts L2 and the MALL
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # 1 GiB read between timed iterations (outside the timed region) evicts L2 and the MALL. A read
+    # leaves clean lines behind; a write would leave dirty ones whose write-back lands in the timed call.
+    flush_buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
 
     def flush():
-        flush_buf.fill_(1)
+        flush_buf.sum()
 
     def timed(fn, reps, cold=True):
         """Median and min (ms) of ``reps`` calls, each between HIP events on the current stream."""
@@ -374,7 +375,7 @@ def main() -> int:
                                    "+ 4 AttnRes routes", "B": 1, "N": 75600, "grid": [21, 45, 80], "H": 32, "D": 64,
                        "route_C": 2048, "route_S": 4, "parallelism": "single GPU"},
             "timing": "per call: median (and min) over the timed steps, HIP events on the library's stream; legs: "
-                      "median and min of repeated calls, a 1 GiB write before each outside the timed region",
+                      "median and min of repeated calls, a 1 GiB read before each outside the timed region",
             "linear_hbm_gbs": lin_gbs,
             "linear_hbm_frac": lin_gbs / HBM_PEAK_GBS,
             "linear_ms": lin_ms,
