@@ -45,6 +45,11 @@
  *   ksum_out == ksum_in in hla_linear_attn_chunked and hla_linear_attn_causal,
  *   and dkv_in == dkv_out, dksum_in == dksum_out in
  *   hla_linear_attn_chunked_backward.
+ * - Sizes: B, N, H >= 1 and B * H <= 65535 (a (batch, head) pair indexes a
+ *   launch grid dimension); larger products are HLA_ERR_INVALID_ARG. The
+ *   linear calls also reject a plan whose work-groups per batch element
+ *   (chunks x slabs x head groups) exceed 2^31 - 1, reachable only with very
+ *   short chunks of very long sequences.
  * - Numbers: HLA_BF16 tensors hold bfloat16 values, HLA_F32 tensors float.
  *   States, key sums, router queries and RoPE tables are always float.
  *   Arithmetic is float32 throughout; bf16 outputs are rounded to nearest

@@ -3,7 +3,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
+#include <climits>
 
 #include "hla_internal.h"
 
@@ -57,12 +59,21 @@ RopeArgs make_rope(const hla_rope3d *r) {
   return ra;
 }
 
+// (batch, head) pairs index the second dimension of the launch grids, whose
+// limit is 65 535; token indices fit in 31 bits and element offsets of a
+// [B][N][H][64] tensor in 63.
+constexpr long long kMaxBatchHeads = 65535;
+
 bool shape_ok(int B, int N, int H) {
   if (B <= 0 || N <= 0 || H <= 0) return false;
-  // every element offset of a [B][N][H][64] tensor fits in 63 bits and every
-  // token index in 31 bits; grid dimensions fit in 31 bits
-  if ((long long)B * H > (1LL << 30)) return false;
+  if ((long long)B * H > kMaxBatchHeads) return false;
   return true;
+}
+
+// the first grid dimension of the linear kernels, (chunk, slab or part, head
+// group), within 31 bits (only very short chunks of very long sequences reach it)
+bool plan_ok(const LinearPlan &p) {
+  return (long long)p.n_chunks * std::max(p.slabs_per_chunk, p.apply_per_chunk) * p.ngroups <= INT_MAX;
 }
 
 hla_status linear_common(int dtv, int B, int N, int H, int D, int chunk_tokens, const void *q, const void *k,
@@ -78,6 +89,7 @@ hla_status linear_common(int dtv, int B, int N, int H, int D, int chunk_tokens, 
   if (D != kD) return HLA_ERR_UNSUPPORTED;
   if (!rope_valid(rope, N, D)) return HLA_ERR_INVALID_ARG;
   const LinearPlan plan = plan_linear(B, N, H, chunk_tokens);
+  if (!plan_ok(plan)) return HLA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < plan.total_bytes) return HLA_ERR_WORKSPACE;
   LinearArgs a;
   a.B = B;
@@ -116,6 +128,7 @@ hla_status linear_bwd_common(int dtv, int B, int N, int H, int D, int chunk_toke
   if (!rope_valid(rope, N, D)) return HLA_ERR_INVALID_ARG;
   if (dtv != HLA_BF16) return HLA_ERR_UNSUPPORTED;
   const LinearPlan plan = plan_linear_backward(B, N, H, chunk_tokens);
+  if (!plan_ok(plan)) return HLA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < plan.total_bytes) return HLA_ERR_WORKSPACE;
   LinearBwdArgs a;
   a.B = B;
@@ -266,6 +279,7 @@ hla_status hla_linear_attn_causal(hla_dtype dt, int B, int N, int H, int D, cons
   a.rope = make_rope(rope);
   if (a.rope.enabled && !a.rope.aligned) return HLA_ERR_UNSUPPORTED;
   const LinearPlan plan = plan_linear_causal(B, N, H);
+  if (!plan_ok(plan)) return HLA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < plan.total_bytes) return HLA_ERR_WORKSPACE;
   a.eps = eps;
   a.kv_in = kv_in;

@@ -116,6 +116,10 @@ def test_linear_validation(L):
     assert _linear(L, o=None) == E.HLA_ERR_INVALID_ARG
     assert _linear(L, N=0) == E.HLA_ERR_INVALID_ARG
     assert _linear(L, B=-1) == E.HLA_ERR_INVALID_ARG
+    # (batch, head) pairs index a launch grid dimension: at most 65 535 of them
+    assert _linear(L, B=256, H=256) == E.HLA_ERR_INVALID_ARG
+    assert _linear(L, B=65536) == E.HLA_ERR_INVALID_ARG
+    assert _linear(L, B=5, H=13107, ws=None) == E.HLA_ERR_WORKSPACE  # 65 535 pairs pass the shape check
     assert _linear(L, D=128) == E.HLA_ERR_UNSUPPORTED
     assert _linear(L, dt=7) == E.HLA_ERR_UNSUPPORTED
     assert _linear(L, eps=-1.0) == E.HLA_ERR_INVALID_ARG
@@ -140,6 +144,9 @@ def test_chunked_validation(L):
 
     assert call(chunk=0) == E.HLA_ERR_INVALID_ARG
     assert call(chunk=-3) == E.HLA_ERR_INVALID_ARG
+    # one-token chunks of 2^30 tokens and 32 heads: 2^33 work-groups per batch element
+    assert L.hla_linear_attn_chunked(0, 1, 1 << 30, 32, 64, 1, FAKE, FAKE, FAKE, None, None, 1e-6, None, None,
+                                     None, None, FAKE, FAKE, 1 << 62, None) == E.HLA_ERR_INVALID_ARG
     assert call(kv_in=FAKE) == E.HLA_ERR_INVALID_ARG  # ksum_in missing
     assert call(ks_out=FAKE) == E.HLA_ERR_INVALID_ARG  # kv_out missing
     assert call(ws_bytes=16) == E.HLA_ERR_WORKSPACE
@@ -211,6 +218,8 @@ def test_anchor_validation(L):
     assert call(D=32) == E.HLA_ERR_UNSUPPORTED
     assert call(ws=None) == E.HLA_ERR_WORKSPACE
     assert call(ws_bytes=64 * 64 * 2 - 1) == E.HLA_ERR_WORKSPACE
+    assert L.hla_softmax_anchor(0, 2, 8, 32768, 64, FAKE, FAKE, FAKE, None, 0.125, FAKE, FAKE, 1 << 40,
+                                None) == E.HLA_ERR_INVALID_ARG  # 65 536 (batch, head) pairs
 
 
 def test_anchor_backward_validation(L):
