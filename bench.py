@@ -88,14 +88,14 @@ def _traffic(kernel: str, grid: int, src_hash: str):
 _CPU_INPUTS = {}
 
 
-def _cpu_linear_head(h):
+def _cpu_linear_head(job):
     import oracle
     import synth
 
-    w = synth.HYBRID_LINEAR[0]
-    x = _CPU_INPUTS["linear"]
+    name, h = job
+    w, x = _CPU_INPUTS[name]
     f = {k: synth.to_f64(v[:, :, h:h + 1]) for k, v in x.items()}
-    oracle.linear_attention(f["q"], f["k"], f["v"], f["g"], oracle.Rope3D(w.grid), eps=w.eps)
+    oracle.linear_attention(f["q"], f["k"], f["v"], f.get("g"), oracle.Rope3D(w.grid), eps=w.eps)
     return h
 
 
@@ -124,7 +124,8 @@ def cpu_baseline(anchor_rows: int = 16384, route_tokens: int = 75600):
     Times, on the seeded inputs of the hybrid 720p/5s group: the gated linear layer on all 32
     heads (value: tokens/s of one layer), one AttnRes route (``route_tokens`` tokens, scaled to
     the full route), and ``anchor_rows`` query rows of one anchor head against all keys,
-    extrapolated to the 32 heads and all rows.
+    extrapolated to the 32 heads and all rows; then the cond/uncond pair layer and the fp32
+    1024-token layer in full.
     """
     import multiprocessing as mp
 
@@ -135,7 +136,10 @@ def cpu_baseline(anchor_rows: int = 16384, route_tokens: int = 75600):
     w = synth.HYBRID_LINEAR[0]
     aw = synth.HYBRID_ANCHOR
     rw = synth.HYBRID_ROUTES[0]
-    _CPU_INPUTS["linear"] = w.draw()
+    _CPU_INPUTS["linear"] = (w, w.draw())
+    extra = (synth.LINEAR_CFGPAIR_N32760, synth.LINEAR_F32_N1024)
+    for e in extra:
+        _CPU_INPUTS[e.name] = (e, e.draw())
     a = aw.draw()
     _CPU_INPUTS["anchor"] = {k: synth.to_f64(v[:, :, 0:1]) for k, v in a.items()}
     _CPU_INPUTS["anchor"]["scale"] = aw.scale
@@ -149,8 +153,13 @@ def cpu_baseline(anchor_rows: int = 16384, route_tokens: int = 75600):
     try:
         with mp.get_context("fork").Pool(procs) as pool:
             t0 = time.perf_counter()
-            pool.map(_cpu_linear_head, range(w.H))
+            pool.map(_cpu_linear_head, [("linear", h) for h in range(w.H)])
             lin_s = time.perf_counter() - t0
+            extra_s = {}
+            for e in extra:
+                t0 = time.perf_counter()
+                pool.map(_cpu_linear_head, [(e.name, h) for h in range(e.H)])
+                extra_s[e.name] = time.perf_counter() - t0
             nrow = min(anchor_rows, aw.N)
             t0 = time.perf_counter()
             pool.map(_cpu_anchor_rows, [(i, min(nrow, i + 1024)) for i in range(0, nrow, 1024)])
@@ -184,8 +193,11 @@ def cpu_baseline(anchor_rows: int = 16384, route_tokens: int = 75600):
         "sample": (f"fp64 numpy oracle in {procs} worker processes: all {w.H} heads of one 720p/5s gated linear "
                    f"layer ({lin_s:.1f} s, value), one AttnRes route over {ntok} of {rw.T} tokens "
                    f"({route_sample_s:.1f} s), and {nrow} query rows of one anchor head against all {aw.N} keys "
-                   f"({anc_sample_s:.1f} s)"),
+                   f"({anc_sample_s:.1f} s); also the cond/uncond pair layer (B=2, N=32760, "
+                   f"{extra_s[extra[0].name]:.1f} s) and the fp32 1024-token layer ({extra_s[extra[1].name]:.2f} s)"),
         "linear_layer_s": lin_s,
+        "other_linear_configs": {e.name: {"s": extra_s[e.name], "tokens_per_s": e.B * e.N / extra_s[e.name]}
+                                 for e in extra},
         "route_s": route_s,
         "anchor_s_extrapolated": anc_s,
         "anchor_extrapolation": f"x{aw.N / nrow:.3g} rows, x{aw.H} heads",
