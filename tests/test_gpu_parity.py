@@ -222,6 +222,18 @@ def test_linear_edge_cases_and_determinism():
     # zero-angle tables reduce to no RoPE
     zero = [np.tile(np.array([1.0, 0.0], np.float32), (n, d // 2, 1)) for n, d in zip(grid, (16, 24, 24))]
     assert torch.equal(run_linear(x, grid, rope_tables=zero), run_linear(x, None))
+    # a head whose keys are all negative has an empty state and key sum: o = 0 / (0 + eps) = 0 exactly,
+    # in every form (bidirectional, chunked, token-causal), and the other head is untouched
+    k = x["k"].copy()
+    k[:, :, 0] |= np.uint16(0x8000)
+    xk = dict(x, k=k)
+    for o in (run_linear(xk, grid), run_linear(xk, grid, chunk=300),
+              hla.hla_linear_attn_causal(*(dev(xk[n]) for n in "qkv"), None, hla.Rope3D(grid))):
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(o[:, :, 0]).item() == 0
+    assert torch.equal(run_linear(xk, grid)[:, :, 1], base[:, :, 1])
+    # zero values: o = 0 exactly
+    assert torch.count_nonzero(run_linear(dict(x, v=np.zeros_like(x["v"])), grid)).item() == 0
 
 
 # ----------------------------------------------------------------------------
