@@ -22,6 +22,8 @@
 // partial states are ~2% on top.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace hla {
@@ -424,26 +426,30 @@ __global__ __launch_bounds__(256) void la_scan_kernel(ScanArgs a) {
   float *pre = a.prefix + (size_t)bh * a.n_chunks * kStateFloats + idx;
   // Slabs are summed in index order from zero, then added to the running state,
   // chunk by chunk in scan order. With eight or more slabs per chunk their loads
-  // go out sixteen at a time with no store between them (indices past the last
-  // slab repeat it and are not added). With fewer, the (chunk, slab) partials
-  // are loaded sixteen at a time across chunks before any of them is added: a
-  // prefix store could otherwise be taken to alias the next chunk's partials,
-  // one memory round trip per chunk.
+  // go out in batches of sixteen (eight below sixteen slabs) with no store
+  // between them; indices past the last slab repeat it and are not added. With
+  // fewer, the (chunk, slab) partials are loaded sixteen at a time across chunks
+  // before any of them is added: a prefix store could otherwise be taken to
+  // alias the next chunk's partials, one memory round trip per chunk.
   const int spc = a.slabs_per_chunk;
+  auto chunk_sum = [&](const float *pc, auto width_c) {
+    constexpr int W = decltype(width_c)::value;
+    float s = 0.f;
+    for (int i = 0; i < spc; i += W) {
+      float x[W];
+#pragma unroll
+      for (int j = 0; j < W; ++j) x[j] = pc[(size_t)min(i + j, spc - 1) * kStateFloats];
+#pragma unroll
+      for (int j = 0; j < W; ++j)
+        if (i + j < spc) s += x[j];
+    }
+    return s;
+  };
   if (spc >= 8) {
     for (int ci = 0; ci < a.n_chunks; ++ci) {
       const int c = a.reverse ? a.n_chunks - 1 - ci : ci;
       const float *pc = p + (size_t)c * spc * kStateFloats;
-      float s = 0.f;
-      for (int i = 0; i < spc; i += 16) {
-        float x[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = pc[(size_t)min(i + j, spc - 1) * kStateFloats];
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (i + j < spc) s += x[j];
-      }
-      run += s;
+      run += spc >= 16 ? chunk_sum(pc, std::integral_constant<int, 16>{}) : chunk_sum(pc, std::integral_constant<int, 8>{});
       pre[(size_t)c * kStateFloats] = run;
     }
   } else {
