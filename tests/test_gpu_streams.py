@@ -1,0 +1,69 @@
+"""Every call runs on the stream it is given.
+
+The inputs are produced on a side stream behind a long matrix product, and the
+library call is issued on that side stream with no other synchronisation. Had
+any kernel run on another stream it would read the inputs before they exist
+(they start as uninitialised memory); on the given stream it reads them in
+order, and the outputs equal those of the same call on the default stream
+bitwise. Streams keep the default priority.
+"""
+import pytest
+import torch
+
+import synth
+from softmax_attention_relu_amd import hla
+
+from gpu_common import dev, say
+
+pytestmark = pytest.mark.gpu
+
+B, N, H = 1, 1000, 4
+GRID = (10, 10, 10)
+
+
+def delayed_copies(side, tensors):
+    """Copies of ``tensors`` made on ``side`` after a long product queued there first."""
+    with torch.cuda.stream(side):
+        a = torch.randn((4096, 4096), device="cuda")
+        for _ in range(8):
+            a = a @ a
+            a = a / a.abs().max()
+        out = [torch.empty_like(t) for t in tensors]
+        for o, t in zip(out, tensors):
+            o.copy_(t)
+    return out
+
+
+def test_linear_forms_on_a_side_stream():
+    say("[streams] linear, chunked, causal")
+    x = [dev(synth.randn(950, (B, N, H, 64), stream=i)) for i in range(4)]
+    rope = hla.Rope3D(GRID)
+    ref = hla.hla_linear_attn(*x, rope)
+    ref_c = hla.hla_linear_attn_chunked(x[0], x[1], x[2], 300, x[3], rope)
+    ref_t = hla.hla_linear_attn_causal(*x, rope)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    xs = delayed_copies(side, x)
+    with torch.cuda.stream(side):
+        o = hla.hla_linear_attn(*xs, rope, stream=side)
+        oc = hla.hla_linear_attn_chunked(xs[0], xs[1], xs[2], 300, xs[3], rope, stream=side)
+        ot = hla.hla_linear_attn_causal(*xs, rope, stream=side)
+    side.synchronize()
+    assert torch.equal(o, ref) and torch.equal(oc, ref_c) and torch.equal(ot, ref_t)
+
+
+def test_anchor_and_route_on_a_side_stream():
+    say("[streams] anchor, route")
+    x = [dev(synth.randn(951, (B, N, H, 64), stream=i)) for i in range(4)]
+    srcs = [dev(synth.randn(952, (B, N, 256), stream=i)) for i in range(4)]
+    w = dev(synth.randn(953, (256,), std=0.02, dtype="f32"))
+    ref = hla.hla_softmax_anchor(*x)
+    ref_h, ref_a = hla.hla_attnres_route(srcs, w, None, alpha=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    xs = delayed_copies(side, x + srcs)
+    with torch.cuda.stream(side):
+        o = hla.hla_softmax_anchor(*xs[:4], stream=side)
+        h, al = hla.hla_attnres_route(xs[4:], w, None, alpha=True, stream=side)
+    side.synchronize()
+    assert torch.equal(o, ref) and torch.equal(h, ref_h) and torch.equal(al, ref_a)
