@@ -48,7 +48,18 @@ struct BwdArgs {
   RopeArgs rope;
   float eps;
   const float *state;  // [B*H][n_chunks][kStateFloats]: KV_c, ksum_c or G_c, Gz_c
+  // the forward's saved state instead (one chunk): KV [B*H][D][D] in state,
+  // ksum [B*H][D] here; null for the records above
+  const float *ksum;
 };
+
+// The chunk's 64x64 matrix and its key sum (or gradient key sum)
+__device__ __forceinline__ const float *state_matrix(const BwdArgs &a, int bh, int chunk) {
+  return a.ksum ? a.state + (size_t)bh * kD * kD : a.state + ((size_t)bh * a.n_chunks + chunk) * kStateFloats;
+}
+__device__ __forceinline__ const float *state_sum(const BwdArgs &a, int bh, int chunk) {
+  return a.ksum ? a.ksum + (size_t)bh * kD : state_matrix(a, bh, chunk) + kD * kD;
+}
 
 // Lane layout of a step: lane (tl = lane % 32, hf = lane / 32) holds token tl
 // and the 32 dims 32*mb + 16*hf + 8*v + t (mb, v in {0, 1}, t < 8), kept as
@@ -249,7 +260,8 @@ __global__ __launch_bounds__(256, 1) void la_bwd_query_kernel(BwdArgs a) {
   StepRange sr;
   if (!step_range(a, wave, sr)) return;  // no work-group barrier in this kernel
 
-  const float *P = a.state + ((size_t)sr.bh * a.n_chunks + sr.chunk) * kStateFloats;
+  const float *P = state_matrix(a, sr.bh, sr.chunk);
+  const float *Z = state_sum(a, sr.bh, sr.chunk);
   bf16x8_t th[2][4], tlo[2][4], nh[2][4], nlo[2][4];
   state_operands<true>(P, tl, hf, th, tlo);
   state_operands<false>(P, tl, hf, nh, nlo);
@@ -259,7 +271,7 @@ __global__ __launch_bounds__(256, 1) void la_bwd_query_kernel(BwdArgs a) {
 #pragma unroll
     for (int v = 0; v < 2; ++v)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) z[mb][v][t] = P[kD * kD + 32 * mb + 16 * hf + 8 * v + t];
+      for (int t = 0; t < 8; ++t) z[mb][v][t] = Z[32 * mb + 16 * hf + 8 * v + t];
   PieceRope<kRopeMode> pr;
   pr.init(a.rope, hf);
 
@@ -365,7 +377,8 @@ __global__ __launch_bounds__(256, 1) void la_bwd_key_kernel(BwdArgs a) {
   StepRange sr;
   if (!step_range(a, wave, sr)) return;  // no work-group barrier in this kernel
 
-  const float *P = a.state + ((size_t)sr.bh * a.n_chunks + sr.chunk) * kStateFloats;
+  const float *P = state_matrix(a, sr.bh, sr.chunk);
+  const float *Z = state_sum(a, sr.bh, sr.chunk);
   bf16x8_t th[2][4], tlo[2][4], nh[2][4], nlo[2][4];
   state_operands<true>(P, tl, hf, th, tlo);
   state_operands<false>(P, tl, hf, nh, nlo);
@@ -375,7 +388,7 @@ __global__ __launch_bounds__(256, 1) void la_bwd_key_kernel(BwdArgs a) {
 #pragma unroll
     for (int v = 0; v < 2; ++v)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) z[mb][v][t] = P[kD * kD + 32 * mb + 16 * hf + 8 * v + t];
+      for (int t = 0; t < 8; ++t) z[mb][v][t] = Z[32 * mb + 16 * hf + 8 * v + t];
   PieceRope<kRopeMode> pr;
   pr.init(a.rope, hf);
 
@@ -492,20 +505,7 @@ hipError_t launch_linear_backward(const LinearBwdArgs &a, const LinearPlan &p, h
   s.init_copy = nullptr;
   float *state = nullptr;
   hipError_t e;
-  if (a.kv_saved) {
-    // the forward's state, packed into the one record per head of the prefix
-    // ([D*D state | D key sum]) that the build and scan would have written
-    state = reinterpret_cast<float *>(ws + p.prefix_offset);
-    const size_t heads = (size_t)a.B * a.H;
-    e = hipMemcpy2DAsync(state, kStateFloats * sizeof(float), a.kv_saved, kD * kD * sizeof(float),
-                         kD * kD * sizeof(float), heads, hipMemcpyDeviceToDevice, stream);
-    if (e != hipSuccess) return e;
-    e = hipMemcpy2DAsync(state + kD * kD, kStateFloats * sizeof(float), a.ksum_saved, kD * sizeof(float),
-                         kD * sizeof(float), heads, hipMemcpyDeviceToDevice, stream);
-    if (e != hipSuccess) return e;
-  } else if ((e = launch_state_sums(HLA_BF16, s, p, a.ws, stream, &state)) != hipSuccess) {
-    return e;
-  }
+  if (!a.kv_saved && (e = launch_state_sums(HLA_BF16, s, p, a.ws, stream, &state)) != hipSuccess) return e;
 
   BwdArgs qa;
   qa.x0 = reinterpret_cast<const uint16_t *>(a.q);
@@ -523,7 +523,10 @@ hipError_t launch_linear_backward(const LinearBwdArgs &a, const LinearPlan &p, h
   qa.ngroups = p.ngroups;
   qa.rope = a.rope;
   qa.eps = a.eps;
-  qa.state = state;
+  // the query side reads the forward's saved state where it is given (one
+  // chunk), the records of the build and scan otherwise
+  qa.state = a.kv_saved ? a.kv_saved : state;
+  qa.ksum = a.kv_saved ? a.ksum_saved : nullptr;
   BwdArgs ka = qa;
   ka.x0 = reinterpret_cast<const uint16_t *>(a.k);
   ka.x1 = reinterpret_cast<const uint16_t *>(a.v);
@@ -553,6 +556,7 @@ hipError_t launch_linear_backward(const LinearBwdArgs &a, const LinearPlan &p, h
 
   // 4. key side
   ka.state = state;
+  ka.ksum = nullptr;
   launch_bwd(a.rope, false, grid, qa, ka, stream, 1);
   return hipGetLastError();
 }
