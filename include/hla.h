@@ -282,16 +282,23 @@ hla_status hla_linear_attn_chunked_backward(hla_dtype dt, int B, int N, int H, i
  * (SANA-Video 2.0 abstract and summary; textbook scaled dot-product form):
  *   o_i = sigmoid(g_i) * sum_j softmax_j(scale * q_i . k_j) v_j
  * q, k, v, g, o: [B][N][H][D] bf16 (dt must be HLA_BF16); g may be NULL.
- * Products run on bf16 matrix cores with float accumulation and a float
- * online softmax; the probabilities are rounded to bf16 for the P.V product.
- * The softmax subtracts a per-row reference: the running row maximum, or, for
- * the rows of a 32-row group whose bound b_i = scale log2(e) |q_i| max_j |k_j|
- * (Cauchy-Schwarz: no logit exceeds it) is at most 48 in log2 units, b_i itself
- * (softmax does not depend on the reference; the result differs only in
- * rounding). Both paths give the same results up to bf16 rounding.
+ * The P.V product runs on bf16 matrix cores (weights rounded to bf16, float
+ * accumulation). The scores take one of two forms, per group of 512 query rows
+ * of one head:
+ *   - where every row's bound b_i = scale log2(e) |q_i| max_j |k_j| (by
+ *     Cauchy-Schwarz no |scale log2(e) q_i . k_j| exceeds it) is at most 48,
+ *     scale log2(e) |q_i| <= 2^10, max_j |k_j| <= 2^10 and no finite |v| exceeds
+ *     2^40: fp16 matrix-core products of K and of q pre-scaled by
+ *     scale log2(e) (rounded to fp16, 11 significant bits), the weights 2 to
+ *     the power of those products, with no reference subtracted (they stay
+ *     within 2^(+-48));
+ *   - otherwise bf16 products and a float online softmax whose running row
+ *     maximum is refreshed lazily.
+ * Both give the exact result up to rounding of the order of bf16's.
  * ws: device workspace of at least hla_softmax_anchor_workspace(B, N, H, D)
- *     bytes; it receives V transposed per head and the largest squared K norm
- *     of every 64-key block (contents on entry ignored).
+ *     bytes; it receives V transposed per head, K in fp16, and the largest
+ *     squared K norm and largest finite |v| of every 64-key block (contents on
+ *     entry ignored).
  * Errors: INVALID_ARG for null q/k/v/o, B, N or H <= 0, scale not finite and
  * positive; UNSUPPORTED for D != 64 or dt != HLA_BF16; WORKSPACE if ws is NULL
  * or ws_bytes is too small.

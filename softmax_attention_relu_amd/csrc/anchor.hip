@@ -7,7 +7,9 @@
 //   anchor_vt  writes V of each (b, h) transposed, [64 dims][Npad tokens],
 //              tokens zero-padded to a multiple of 64 and permuted inside each
 //              group of 16 so that every matrix-core operand of the P.V product
-//              is one contiguous 16-byte LDS read (see kernel comment).
+//              is one contiguous 16-byte LDS read (see kernel comment); for
+//              the forward it also records each 64-key block's largest K norm
+//              and finite |v|, and writes K in fp16.
 //   anchor_fwd online-softmax attention. A work-group of 16 waves owns 512
 //              query rows of one (b, h); wave w owns 32 rows. Per 64-key tile:
 //                S^T = K Q^T   (A = K rows from LDS, B = Q^T held in registers)
@@ -17,6 +19,10 @@
 //                score registers, rounded to bf16)
 //              K and V^T tiles are double-buffered in LDS; the next tile's
 //              global loads are issued before the current tile's products.
+//              Where a static bound on the logits holds (most inputs), the
+//              scores come from fp16 products of K and Q^T pre-scaled by
+//              scale log2(e), so the weights are exp2 of the products with no
+//              per-score arithmetic before the exponential.
 // At most 128 registers per lane keep every accumulator in VGPRs with four
 // waves per SIMD; the tile's row max is combined across the two lane halves
 // with v_permlane32_swap. On this chip the plain vector ALU work of the
@@ -43,6 +49,10 @@ constexpr int kVRow = kBK + 8;     // bf16 per LDS row of V^T (144 bytes)
 constexpr int kORow = kD + 8;      // bf16 per LDS row of the output stage (144 bytes)
 constexpr float kLazy = 8.0f;      // lazy max threshold, log2 units
 constexpr float kStatic = 48.0f;   // largest static row reference, log2 units
+// bounds for the half-precision scores: c |q_i| <= 2^10, |k_j|^2 <= 2^20, |v| <= 2^40
+constexpr float kHalfQ = 1024.0f;
+constexpr float kHalfK2 = 1048576.0f;
+constexpr float kHalfV = 1099511627776.0f;
 constexpr int kLateSleep = 4;      // the late wave group's start offset, units of 64 cycles
 constexpr int kVmcnt0 = 0x0F70;    // s_waitcnt immediate: vmcnt(0), other counters free
 constexpr int kWaves = 16;         // waves per work-group, 32 query rows each
@@ -74,7 +84,26 @@ struct VtArgs {
   // [B*H][npad / 64] (the forward's static row reference)
   const uint16_t *k;
   float *kmax2;
+  // optional with kmax2: the largest finite |v| element of each 64-key block
+  // ([B*H][npad / 64]) and K in half precision ([B*H][npad][64], rows past N
+  // zero), for the forward's half-precision scores
+  float *vmax;
+  uint16_t *kh;
 };
+
+// two bf16 -> two fp16 (nearest even; exact for |x| in [2^-14, 65504])
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const _Float16 lo = (_Float16)bf16_lo(w), hi = (_Float16)bf16_hi(w);
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// largest finite |x| of the two bf16 in w as a bf16 bit pattern (0 if neither
+// is finite): a NaN or Inf in v reaches only its own output column, whatever
+// loop the forward takes, so only finite values bound the weights' headroom
+__device__ __forceinline__ uint32_t finite_abs_bits(uint32_t x) { return x < 0x7f80u ? x : 0u; }
+__device__ __forceinline__ uint32_t max_abs_bits(uint32_t w) {
+  return max(finite_abs_bits(w & 0x7fffu), finite_abs_bits((w >> 16) & 0x7fffu));
+}
 
 __global__ __launch_bounds__(256) void anchor_vt_kernel(VtArgs a) {
   __shared__ uint16_t tile[kBK][kD + 2];
@@ -84,6 +113,7 @@ __global__ __launch_bounds__(256) void anchor_vt_kernel(VtArgs a) {
   const int n0 = blockIdx.x * kBK;
   const size_t tok_stride = (size_t)a.H * kD;
   const uint16_t *vp = a.v + (size_t)b * a.N * tok_stride + (size_t)h * kD;
+  uint32_t vm = 0u;  // largest finite |v| of this thread's elements, bf16 bits
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int c = tid + 256 * r;
@@ -91,11 +121,13 @@ __global__ __launch_bounds__(256) void anchor_vt_kernel(VtArgs a) {
     const int n = n0 + key;
     uint4 w = make_uint4(0, 0, 0, 0);
     if (n < a.N) w = load_once_u4(vp + (size_t)n * tok_stride + 8 * dc);
+    vm = max(max(vm, max_abs_bits(w.x)), max(max_abs_bits(w.y), max(max_abs_bits(w.z), max_abs_bits(w.w))));
     uint32_t *dst = reinterpret_cast<uint32_t *>(&tile[key][8 * dc]);
     dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
   }
   if (a.kmax2) {
     __shared__ float wmax[4];
+    __shared__ uint32_t wvm[4];
     float m = 0.f;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -103,12 +135,16 @@ __global__ __launch_bounds__(256) void anchor_vt_kernel(VtArgs a) {
       const int key = c >> 3, dc = c & 7;
       const int n = n0 + key;
       float ss = 0.f;
+      uint4 w = make_uint4(0, 0, 0, 0);
       if (n < a.N) {
-        const uint4 w = load_once_u4(a.k + (vp - a.v) + (size_t)n * tok_stride + 8 * dc);
+        w = load_once_u4(a.k + (vp - a.v) + (size_t)n * tok_stride + 8 * dc);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) ss += bf16_lo(ws[j]) * bf16_lo(ws[j]) + bf16_hi(ws[j]) * bf16_hi(ws[j]);
       }
+      if (a.kh)
+        *reinterpret_cast<uint4 *>(a.kh + ((size_t)bh * a.npad + n) * kD + 8 * dc) =
+            make_uint4(bf16x2_to_f16x2(w.x), bf16x2_to_f16x2(w.y), bf16x2_to_f16x2(w.z), bf16x2_to_f16x2(w.w));
       // the key's eight chunks sit in eight consecutive lanes
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
@@ -118,10 +154,18 @@ __global__ __launch_bounds__(256) void anchor_vt_kernel(VtArgs a) {
     m = fmaxf(m, __shfl_xor(m, 8));
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
-    if ((tid & 63) == 0) wmax[tid >> 6] = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) vm = max(vm, (uint32_t)__shfl_xor((int)vm, o));
+    if ((tid & 63) == 0) {
+      wmax[tid >> 6] = m;
+      wvm[tid >> 6] = vm;
+    }
     __syncthreads();
-    if (tid == 0)
-      a.kmax2[(size_t)bh * (a.npad / kBK) + blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (tid == 0) {
+      const size_t blk = (size_t)bh * (a.npad / kBK) + blockIdx.x;
+      a.kmax2[blk] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+      if (a.vmax) a.vmax[blk] = __uint_as_float(max(max(wvm[0], wvm[1]), max(wvm[2], wvm[3])) << 16);
+    }
   }
   __syncthreads();
   uint16_t *out = a.vt + (size_t)bh * kD * a.npad + n0;
@@ -150,6 +194,10 @@ struct FwdArgs {
   // static row reference (nullable): the largest squared K norm of each 64-key
   // block of the head, [B*H][npad / 64]
   const float *kmax2;
+  // half-precision scores (nullable, with kmax2): the largest finite |v| of each
+  // 64-key block, [B*H][npad / 64], and K in fp16, [B*H][npad][64]
+  const float *vmax;
+  const uint16_t *kh;
   // block-sparse form: key tiles named per (b*H + h, query block), [..][max_blocks]
   const int *blocks, *counts;
   int n_qb, max_blocks;
@@ -163,6 +211,7 @@ struct FwdArgs {
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 // The row sum adds the bf16-rounded P with v_dot2 (two terms per
 // instruction): the normaliser uses the same weights as the P.V product.
@@ -214,28 +263,49 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
   // waits for all loads (the next tile's included) before every tile's first product.
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
-  // Row reference. By Cauchy-Schwarz every logit of row i obeys
-  // c s_ij <= c |q_i| max_j |k_j| =: b_i, so b_i can stand in for the row max:
-  // softmax does not depend on the reference, and with b_i >= the true max no
-  // weight exceeds 1. The true max is >= -b_i, so while b_i <= kStatic the
-  // row's largest weight is >= 2^(-2 kStatic) and nothing underflows; a wave
-  // whose rows all qualify skips the per-tile row max. Otherwise (or without
-  // the key norms) it keeps the running max.
-  bool stat = false;
+  // Static bound. By Cauchy-Schwarz every logit of row i obeys
+  // |c s_ij| <= c |q_i| max_j |k_j| =: b_i. Softmax does not depend on the
+  // reference it subtracts, so while b_i <= kStatic a row needs no running max:
+  // - the gradient preparation subtracts b_i itself (no weight exceeds 1, the
+  //   largest is >= 2^(-2 kStatic), nothing underflows), per wave;
+  // - the forward subtracts nothing and takes the half-precision scores below
+  //   (weights within 2^(+-kStatic)), per work-group.
+  // Otherwise (or without the key norms) the running max.
+  bool stat = false, half_scores = false;
   float mref = -INFINITY, lsum = 0.f;
   if (a.kmax2) {
     __shared__ float wk[WAVES];
+    __shared__ uint32_t wv[WAVES];
+    __shared__ int all_half;
+    if (tid == 0) all_half = 1;
     const int nblk = a.npad / kBK;
     const float *km = a.kmax2 + (size_t)bh * nblk;
+    const float *vx = a.vmax ? a.vmax + (size_t)bh * nblk : nullptr;
+    // maxima of non-negative floats compared as bit patterns: a NaN sorts
+    // above every number and so fails every bound below
     float m = 0.f;
-    for (int i = tid; i < nblk; i += kThreads) m = fmaxf(m, km[i]);
+    uint32_t mv = 0u;
+    for (int i = tid; i < nblk; i += kThreads) {
+      m = fmaxf(m, km[i]);
+      if (vx) mv = max(mv, __float_as_uint(vx[i]));
+    }
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if (lane == 0) wk[wave] = m;
+    for (int o = 1; o < 64; o <<= 1) {
+      m = fmaxf(m, __shfl_xor(m, o));
+      mv = max(mv, (uint32_t)__shfl_xor((int)mv, o));
+    }
+    if (lane == 0) {
+      wk[wave] = m;
+      wv[wave] = mv;
+    }
     __syncthreads();
     m = wk[0];
+    mv = wv[0];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) m = fmaxf(m, wk[w]);
+    for (int w = 1; w < WAVES; ++w) {
+      m = fmaxf(m, wk[w]);
+      mv = max(mv, wv[w]);
+    }
     float qn = 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -244,26 +314,41 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     qn += __shfl_xor(qn, 32);
     const float bnd = a.c * sqrtf(qn) * sqrtf(m);
     stat = __builtin_amdgcn_readfirstlane(__all(bnd <= kStatic)) != 0;
-    if (stat) mref = bnd;
+    if (kPrep && stat) mref = bnd;
+    if (!kPrep && a.kh) {
+      // Half-precision scores, taken by the whole work-group or not at all (the
+      // K tiles it stages are fp16 or bf16): every row static, c |q_i| and
+      // |k_j| small enough that fp16's subnormal range costs nothing, and |v|
+      // small enough that weights up to 2^kStatic cannot overflow O
+      const bool ok = stat && __float_as_uint(a.c * sqrtf(qn)) <= __float_as_uint(kHalfQ) &&
+                      __float_as_uint(m) <= __float_as_uint(kHalfK2) && mv <= __float_as_uint(kHalfV);
+      if (lane == 0 && !__all(ok)) all_half = 0;
+      __syncthreads();
+      half_scores = all_half != 0;
+      if (half_scores) mref = 0.f;
+    }
   }
   // Two wave groups per SIMD (bit 2 of the wave index); the second starts each
   // tile a few hundred cycles late, so the two groups' matrix-core phases fall
   // less on each other's and more on the other group's vector phase.
   const bool late = (__builtin_amdgcn_readfirstlane(wave) & 4) != 0;
 
-  // tile loader: K (64 keys x 8 chunks) and V^T (64 dims x 8 chunks), 16-byte
-  // chunks spread over the work-group; rows past the end of K repeat the last
-  // row (their scores are masked)
+  // tile loader: K (64 keys x 8 chunks, bf16 from the input or fp16 from the
+  // copy) and V^T (64 dims x 8 chunks), 16-byte chunks spread over the
+  // work-group; rows past the end of K repeat the last row (their scores are masked)
   uint4 kreg[kLoads], vreg[kLoads];
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t, auto mode_c) {
     if (tid >= kLoaders) return;
+    constexpr bool kHalf = decltype(mode_c)::value == 2;
+    const uint16_t *ksrc = kHalf ? a.kh + (size_t)bh * a.npad * kD : kp;
+    const size_t kstride = kHalf ? (size_t)kD : tok_stride;
     const int n0 = t * kBK;
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
       const int c = tid + kLoaders * r;
       const int row = c >> 3, ch = c & 7;
       const int n = min(n0 + row, a.N - 1);
-      kreg[r] = *reinterpret_cast<const uint4 *>(kp + (size_t)n * tok_stride + 8 * ch);
+      kreg[r] = *reinterpret_cast<const uint4 *>(ksrc + (size_t)n * kstride + 8 * ch);
       vreg[r] = *reinterpret_cast<const uint4 *>(vtp + (size_t)row * a.npad + n0 + 8 * ch);
     }
   };
@@ -323,20 +408,32 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     }
   };
 
-  // The tile loop, once with the running max and once with the static
-  // reference: separate copies keep each within the register budget. Both run
-  // the same barriers, so the waves of one work-group may take either.
-  auto tile_loop = [&](auto stat_c) {
-    constexpr bool kStat = decltype(stat_c)::value;
+  // The tile loop, in three copies that keep each within the register budget:
+  // kMode 0 running max, 1 static reference, 2 half-precision scores. All run
+  // the same barriers, so the waves of one work-group may take 0 or 1; 2 is
+  // taken by all of its waves or none.
+  auto tile_loop = [&](auto mode_c) {
+    constexpr int kMode = decltype(mode_c)::value;
+    // Q^T scaled by c = scale log2(e) and rounded to fp16 (11 significant
+    // bits against bf16's 8): the products then give the exponents c s_ij
+    // directly, and the weights 2^(c s_ij) need no reference: |c s_ij| <= b_i
+    // <= kStatic keeps them within 2^(+-kStatic)
+    f16x8_t qh[4];
+    if constexpr (kMode == 2) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qh[s][j] = (_Float16)(a.c * (float)qb[s][j]);
+    }
     int t = next(0);
     if (t < ntiles) {
-      load_tile(t);
+      load_tile(t, mode_c);
       store_tile(0);
     }
     __syncthreads();
     for (int buf = 0; t < ntiles; buf ^= 1) {
       const int tnext = next(t + 1);
-      if (tnext < ntiles) load_tile(tnext);
+      if (tnext < ntiles) load_tile(tnext, mode_c);
       if (late) __builtin_amdgcn_s_sleep(kLateSleep);
       if (kSparse && !((own[t >> 5] >> (t & 31)) & 1u)) {  // not named by this wave's block
         if (tnext < ntiles) {
@@ -359,9 +456,13 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8_t kv =
-              *reinterpret_cast<const bf16x8_t *>(&ks[buf][(32 * kb + tl) * kKRow + 16 * s + 8 * half]);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qb[s], sacc[kb], 0, 0, 0);
+          const uint16_t *kr = &ks[buf][(32 * kb + tl) * kKRow + 16 * s + 8 * half];
+          if constexpr (kMode == 2)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8_t *>(kr), qh[s],
+                                                              sacc[kb], 0, 0, 0);
+          else
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(kr), qb[s],
+                                                               sacc[kb], 0, 0, 0);
         }
 
       // mask keys past the end (last tile only)
@@ -375,7 +476,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
               if (t * kBK + 32 * kb + 8 * i + 4 * half + j >= a.N) sacc[kb][4 * i + j] = -INFINITY;
       }
 
-      if constexpr (!kStat) {
+      if constexpr (kMode == 0) {
         // running max, refreshed lazily: rows keep their reference until a tile
         // exceeds it by more than kLazy (log2 units), so weights stay <= 2^kLazy
         // and the O / row-sum rescale is almost never taken
@@ -407,7 +508,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
       for (int kb = 0; kb < 2; ++kb) {
         float p[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], a.c, nm));
+        for (int i = 0; i < 16; ++i)
+          p[i] = __builtin_amdgcn_exp2f(kMode == 2 ? sacc[kb][i] : fmaf(sacc[kb][i], a.c, nm));
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const uint4 w = make_uint4(pack_bf16(p[8 * u + 0], p[8 * u + 1]), pack_bf16(p[8 * u + 2], p[8 * u + 3]),
@@ -441,10 +543,17 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
       t = tnext;
     }
   };
-  if (stat)
-    tile_loop(std::true_type{});
-  else
-    tile_loop(std::false_type{});
+  if constexpr (kPrep) {
+    if (stat)
+      tile_loop(std::integral_constant<int, 1>{});
+    else
+      tile_loop(std::integral_constant<int, 0>{});
+  } else {
+    if (half_scores)
+      tile_loop(std::integral_constant<int, 2>{});
+    else
+      tile_loop(std::integral_constant<int, 0>{});
+  }
 
   // normalise, gate, store: lane holds row tl, dims 32*mb + 8*i + 4*half + j
   const int n = q0 + tl;
@@ -897,7 +1006,8 @@ __global__ __launch_bounds__(256) void anchor_prep_saved_kernel(PrepArgs a) {
 }
 
 hipError_t launch_vt(const void *x, void *xt, int B, int N, int H, int npad, hipStream_t stream,
-                     const void *k = nullptr, float *kmax2 = nullptr) {
+                     const void *k = nullptr, float *kmax2 = nullptr, float *vmax = nullptr,
+                     uint16_t *kh = nullptr) {
   VtArgs va;
   va.v = reinterpret_cast<const uint16_t *>(x);
   va.vt = reinterpret_cast<uint16_t *>(xt);
@@ -906,6 +1016,8 @@ hipError_t launch_vt(const void *x, void *xt, int B, int N, int H, int npad, hip
   va.npad = npad;
   va.k = reinterpret_cast<const uint16_t *>(k);
   va.kmax2 = kmax2;
+  va.vmax = vmax;
+  va.kh = kh;
   hipLaunchKernelGGL(anchor_vt_kernel, dim3(npad / kBK, B * H), dim3(256), 0, stream, va);
   return hipGetLastError();
 }
@@ -1027,19 +1139,35 @@ size_t anchor_sparse_lds_bytes(int N) {
   return nwords * (1 + kWaves / (kSparseQBlock / 32)) * sizeof(uint32_t);
 }
 
-// forward workspace: V^T (bf16, [B*H][64][npad]), then the key-block norms
-// (fp32, [B*H][npad / 64])
-size_t anchor_workspace_bytes(int B, int N, int H) {
+namespace {
+// forward workspace: V^T (bf16, [B*H][64][npad]), the key-block norms and
+// value maxima (fp32, [B*H][npad / 64] each), K in fp16 ([B*H][npad][64])
+struct FwdLayout {
+  size_t kmax2, vmax, kh, total;
+};
+FwdLayout fwd_layout(int B, int N, int H) {
   const size_t npad = ((size_t)N + kBK - 1) / kBK * kBK;
-  return align256((size_t)B * H * kD * npad * sizeof(uint16_t)) + (size_t)B * H * (npad / kBK) * sizeof(float);
+  const size_t t = align256((size_t)B * H * kD * npad * sizeof(uint16_t));
+  const size_t blk = align256((size_t)B * H * (npad / kBK) * sizeof(float));
+  FwdLayout l;
+  l.kmax2 = t;
+  l.vmax = t + blk;
+  l.kh = t + 2 * blk;
+  l.total = l.kh + (size_t)B * H * kD * npad * sizeof(uint16_t);
+  return l;
 }
+}  // namespace
+
+size_t anchor_workspace_bytes(int B, int N, int H) { return fwd_layout(B, N, H).total; }
 
 hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   const int heads = a.B * a.H;
   const int npad = (a.N + kBK - 1) / kBK * kBK;
-  float *kmax2 = reinterpret_cast<float *>(reinterpret_cast<char *>(a.ws) +
-                                           align256((size_t)heads * kD * npad * sizeof(uint16_t)));
-  hipError_t e = launch_vt(a.v, a.ws, a.B, a.N, a.H, npad, stream, a.k, kmax2);
+  const FwdLayout l = fwd_layout(a.B, a.N, a.H);
+  char *ws = reinterpret_cast<char *>(a.ws);
+  float *kmax2 = reinterpret_cast<float *>(ws + l.kmax2), *vmax = reinterpret_cast<float *>(ws + l.vmax);
+  uint16_t *kh = reinterpret_cast<uint16_t *>(ws + l.kh);
+  hipError_t e = launch_vt(a.v, a.ws, a.B, a.N, a.H, npad, stream, a.k, kmax2, vmax, kh);
   if (e != hipSuccess) return e;
 
   FwdArgs fa;
@@ -1058,6 +1186,8 @@ hipError_t launch_anchor(const AnchorArgs &a, hipStream_t stream) {
   fa.max_blocks = a.max_blocks;
   fa.lse_out = a.lse;
   fa.kmax2 = kmax2;
+  fa.vmax = vmax;
+  fa.kh = kh;
   if (a.blocks) {
     fa.n_qb = (a.N + kSparseQBlock - 1) / kSparseQBlock;
     hipLaunchKernelGGL((anchor_fwd_kernel<kWaves, kMinWaves, true, false>),

@@ -93,7 +93,8 @@ def test_workspace_sizes(L):
     assert hla.hla_linear_attn_chunked_workspace(2, 999, 3, 64, 999) == hla.hla_linear_attn_workspace(2, 999, 3, 64)
     wa = hla.hla_softmax_anchor_workspace(1, 75600, 32, 64)
     vt = 32 * 64 * 75648 * 2  # V^T padded to 64 tokens
-    assert wa == -(-vt // 256) * 256 + 32 * (75648 // 64) * 4  # then one K norm per 64-key block
+    blk = -(-32 * (75648 // 64) * 4 // 256) * 256  # one K norm (then one |v| maximum) per 64-key block
+    assert wa == -(-vt // 256) * 256 + 2 * blk + vt  # then K in fp16, padded like V^T
 
 
 def _rope(grid=(2, 2, 2), bands=(16, 24, 24)):

@@ -266,6 +266,30 @@ def test_anchor_large_logits():
     assert normwise(got, ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("q_std", [1.0, 2.0])
+def test_anchor_half_and_bf16_score_paths(q_std):
+    """The forward's two loops: half-precision scores where the static logit bound holds and |q|, |k|,
+    |v| are within range, the bf16 running max otherwise. Power-of-two factors leave the exact result
+    unchanged but move the inputs across the range bounds: v * 2^44 (|v| > 2^40), and k * 2^11 with
+    q * 2^-11 (|k| > 2^10, same logits). Each output is checked against the oracle; that each factor
+    changed the loop shows in the bits (the same loop would give exactly the scaled output). q_std 2
+    puts the bound near its limit (b up to ~40 in log2 units)."""
+    x = {nm: synth.randn(610, (1, 2000, 2, 64), std=q_std if nm == "q" else 1.0, stream=i)
+         for i, nm in enumerate("qkvg")}
+    f = {k: synth.to_f64(v) for k, v in x.items()}
+    ref = oracle.softmax_anchor(f["q"], f["k"], f["v"], f["g"], scale=0.125)
+    d = {k: dev(v) for k, v in x.items()}
+    half = hla.hla_softmax_anchor(d["q"], d["k"], d["v"], d["g"], 0.125)
+    big_v = hla.hla_softmax_anchor(d["q"], d["k"], d["v"] * 2.0 ** 44, d["g"], 0.125)
+    big_k = hla.hla_softmax_anchor(d["q"] * 2.0 ** -11, d["k"] * 2.0 ** 11, d["v"], d["g"], 0.125)
+    torch.cuda.synchronize()
+    assert normwise(host(half), ref) <= TOL_BF16
+    assert normwise(host(big_v) * 2.0 ** -44, ref) <= TOL_BF16
+    assert normwise(host(big_k), ref) <= TOL_BF16
+    assert not torch.equal(big_v, half * 2.0 ** 44)
+    assert not torch.equal(big_k, half)
+
+
 def test_anchor_full_size_sampled_rows():
     w = synth.HYBRID_ANCHOR
     say(f"[parity] {w.name}: N={w.N} H={w.H}")
