@@ -431,6 +431,12 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
       store_tile(0);
     }
     __syncthreads();
+    // Code placement: the half-precision loop below runs 39.3 ms per 720p/5s
+    // call when its first instruction sits 40 or 44 bytes past a 64-byte
+    // boundary and 41.0-42.7 ms at the other 4-byte offsets (same instructions,
+    // bitwise equal output). These no-ops, executed once, put it at 44 with
+    // this compiler; tests/test_anchor_placement.py checks the offset.
+    if constexpr (kMode == 2) asm volatile("s_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0");
     for (int buf = 0; t < ntiles; buf ^= 1) {
       const int tnext = next(t + 1);
       if (tnext < ntiles) load_tile(tnext, mode_c);
