@@ -5,7 +5,8 @@ tests/test_oracle.py; parity against the pages is unpinned, as they give no
 pattern). Cases: random patterns with empty lists, entries that name nothing,
 repeated entries, counts beyond max_blocks and negative counts, ragged query
 and key blocks, and work-groups whose four query blocks name different tiles;
-every key block named, which must equal the dense kernel bit for bit; and the
+every key block named, which must equal the dense kernel bit for bit; both
+score loops (half precision and bf16 running max) on one pattern; and the
 720p/5s local-window pattern on sampled rows.
 """
 import numpy as np
@@ -70,6 +71,25 @@ def test_sparse_anchor_random_patterns(N, B, H, gated):
     # rows of query blocks that name no key give exactly zero
     empty = ref == 0
     assert np.all(o[empty] == 0)
+
+
+def test_sparse_anchor_both_score_loops():
+    """The sparse form takes the half-precision scores or the bf16 running max like the dense one: v * 2^44
+    (beyond the |v| bound) changes the loop, which shows in the bits, and both outputs meet the bar."""
+    B, N, H = 1, 700, 2
+    rng = np.random.default_rng(941)
+    x = {nm: synth.randn(941, (B, N, H, 64), stream=i) for i, nm in enumerate("qkvg")}
+    blocks, counts = random_pattern(rng, B, H, N, 6)
+    f = {k: synth.to_f64(v) for k, v in x.items()}
+    ref = oracle.softmax_anchor_block_sparse(f["q"], f["k"], f["v"], blocks, np.clip(counts, 0, 6), f["g"], 0.125)
+    d = {k: dev(v) for k, v in x.items()}
+    bl, ct = torch.from_numpy(blocks).cuda(), torch.from_numpy(counts).cuda()
+    half = hla.hla_softmax_anchor_block_sparse(d["q"], d["k"], d["v"], bl, ct, d["g"], 0.125)
+    big = hla.hla_softmax_anchor_block_sparse(d["q"], d["k"], d["v"] * 2.0 ** 44, bl, ct, d["g"], 0.125)
+    torch.cuda.synchronize()
+    assert normwise(host(half), ref) <= TOL_BF16
+    assert normwise(host(big) * 2.0 ** -44, ref) <= TOL_BF16
+    assert not torch.equal(big, half * 2.0 ** 44)
 
 
 def test_sparse_anchor_full_pattern_equals_dense():
