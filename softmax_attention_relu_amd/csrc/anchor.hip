@@ -266,11 +266,9 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
   // Static bound. By Cauchy-Schwarz every logit of row i obeys
   // |c s_ij| <= c |q_i| max_j |k_j| =: b_i. Softmax does not depend on the
   // reference it subtracts, so while b_i <= kStatic a row needs no running max:
-  // - the gradient preparation subtracts b_i itself (no weight exceeds 1, the
-  //   largest is >= 2^(-2 kStatic), nothing underflows), per wave;
-  // - the forward subtracts nothing and takes the half-precision scores below
-  //   (weights within 2^(+-kStatic)), per work-group.
-  // Otherwise (or without the key norms) the running max.
+  // it subtracts nothing and takes the half-precision scores below (weights
+  // within 2^(+-kStatic)), decided per work-group. Otherwise (or without the
+  // key norms) the running max.
   bool stat = false, half_scores = false;
   float mref = -INFINITY, lsum = 0.f;
   if (a.kmax2) {
@@ -314,8 +312,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     qn += __shfl_xor(qn, 32);
     const float bnd = a.c * sqrtf(qn) * sqrtf(m);
     stat = __builtin_amdgcn_readfirstlane(__all(bnd <= kStatic)) != 0;
-    if (kPrep && stat) mref = bnd;
-    if (!kPrep && a.kh) {
+    if (a.kh) {
       // Half-precision scores, taken by the whole work-group or not at all (the
       // K tiles it stages are fp16 or bf16): every row static, c |q_i| and
       // |k_j| small enough that fp16's subnormal range costs nothing, and |v|
@@ -408,10 +405,9 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     }
   };
 
-  // The tile loop, in three copies that keep each within the register budget:
-  // kMode 0 running max, 1 static reference, 2 half-precision scores. All run
-  // the same barriers, so the waves of one work-group may take 0 or 1; 2 is
-  // taken by all of its waves or none.
+  // The tile loop, in two copies that keep each within the register budget:
+  // kMode 0 running max (bf16 scores), 2 half-precision scores. A work-group's
+  // waves all take the same one (its K tiles are staged in one format).
   auto tile_loop = [&](auto mode_c) {
     constexpr int kMode = decltype(mode_c)::value;
     // Q^T scaled by c = scale log2(e) and rounded to fp16 (11 significant
@@ -435,8 +431,12 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
     // call when its first instruction sits 40 or 44 bytes past a 64-byte
     // boundary and 41.0-42.7 ms at the other 4-byte offsets (same instructions,
     // bitwise equal output). These no-ops, executed once, put it at 44 with
-    // this compiler; tests/test_anchor_placement.py checks the offset.
+    // this compiler in the forward and in the gradient preparation (whose code
+    // before the loop differs); tests/test_anchor_placement.py checks both.
     if constexpr (kMode == 2) asm volatile("s_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0");
+    if constexpr (kMode == 2 && kPrep)
+      asm volatile("s_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0\n\t"
+                   "s_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0\n\ts_nop 0");
     for (int buf = 0; t < ntiles; buf ^= 1) {
       const int tnext = next(t + 1);
       if (tnext < ntiles) load_tile(tnext, mode_c);
@@ -549,17 +549,10 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void anchor_fwd_kernel(FwdArgs a)
       t = tnext;
     }
   };
-  if constexpr (kPrep) {
-    if (stat)
-      tile_loop(std::integral_constant<int, 1>{});
-    else
-      tile_loop(std::integral_constant<int, 0>{});
-  } else {
-    if (half_scores)
-      tile_loop(std::integral_constant<int, 2>{});
-    else
-      tile_loop(std::integral_constant<int, 0>{});
-  }
+  if (half_scores)
+    tile_loop(std::integral_constant<int, 2>{});
+  else
+    tile_loop(std::integral_constant<int, 0>{});
 
   // normalise, gate, store: lane holds row tl, dims 32*mb + 8*i + 4*half + j
   const int n = q0 + tl;
@@ -1032,9 +1025,10 @@ hipError_t launch_vt(const void *x, void *xt, int B, int N, int H, int npad, hip
 
 namespace {
 // gradient workspace: V^T, Q^T, dY^T, K^T (bf16, [B*H][64][npad]), dY (bf16, the
-// layout of q), L and Delta (fp32, [B*H][N]), the key-block norms of the preparation forward
+// layout of q), L and Delta (fp32, [B*H][N]), then for the preparation forward the
+// key-block norms and value maxima (fp32, [B*H][npad / 64]) and K in fp16 ([B*H][npad][64])
 struct BwdLayout {
-  size_t vt, qt, dyt, kt, dy, lse, delta, kmax2, total;
+  size_t vt, qt, dyt, kt, dy, lse, delta, kmax2, vmax, kh, total;
 };
 BwdLayout bwd_layout(int B, int N, int H) {
   const size_t npad = ((size_t)N + kBK - 1) / kBK * kBK;
@@ -1048,7 +1042,9 @@ BwdLayout bwd_layout(int B, int N, int H) {
   l.lse = l.dy + align256((size_t)B * N * H * kD * sizeof(uint16_t));
   l.delta = l.lse + align256((size_t)B * H * N * sizeof(float));
   l.kmax2 = l.delta + align256((size_t)B * H * N * sizeof(float));
-  l.total = l.kmax2 + align256((size_t)B * H * (npad / kBK) * sizeof(float));
+  l.vmax = l.kmax2 + align256((size_t)B * H * (npad / kBK) * sizeof(float));
+  l.kh = l.vmax + align256((size_t)B * H * (npad / kBK) * sizeof(float));
+  l.total = l.kh + t;
   return l;
 }
 }  // namespace
@@ -1086,9 +1082,12 @@ hipError_t launch_anchor_backward(const AnchorBwdArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(anchor_prep_saved_kernel, dim3((unsigned)((pa.rows + 31) / 32)), dim3(256), 0, stream, pa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
-    float *kmax2 = reinterpret_cast<float *>(ws + l.kmax2);
-    if ((e = launch_vt(a.v, vt, a.B, a.N, a.H, npad, stream, a.k, kmax2)) != hipSuccess) return e;
+    float *kmax2 = reinterpret_cast<float *>(ws + l.kmax2), *vmax = reinterpret_cast<float *>(ws + l.vmax);
+    uint16_t *kh = reinterpret_cast<uint16_t *>(ws + l.kh);
+    if ((e = launch_vt(a.v, vt, a.B, a.N, a.H, npad, stream, a.k, kmax2, vmax, kh)) != hipSuccess) return e;
     fa.kmax2 = kmax2;
+    fa.vmax = vmax;
+    fa.kh = kh;
     // preparation: the forward with its epilogue writing dG, dY, L, Delta
     fa.q = reinterpret_cast<const uint16_t *>(a.q);
     fa.k = reinterpret_cast<const uint16_t *>(a.k);

@@ -1,4 +1,5 @@
-"""Where the anchor forward's half-precision tile loop sits in the built library.
+"""Where the anchor's half-precision tile loop sits in the built library (the forward
+and the gradient preparation, the same loop with other code before it).
 
 On the GPU its speed depends on the loop's code placement: 39.3 ms per 720p/5s
 call when the loop's first instruction sits 40 or 44 bytes past a 64-byte
@@ -17,7 +18,9 @@ import pytest
 from softmax_attention_relu_amd import build
 
 LLVM = "/opt/rocm/llvm/bin"
-KERNEL = "_ZN3hla12_GLOBAL__N_117anchor_fwd_kernelILi16ELi4ELb0ELb0EEEvNS0_7FwdArgsE"
+# the dense forward and the gradient preparation (the same loop, other code before it)
+KERNELS = ["_ZN3hla12_GLOBAL__N_117anchor_fwd_kernelILi16ELi4ELb0ELb0EEEvNS0_7FwdArgsE",
+           "_ZN3hla12_GLOBAL__N_117anchor_fwd_kernelILi16ELi4ELb0ELb1EEEvNS0_7FwdArgsE"]
 GOOD = (40, 44)
 
 
@@ -45,13 +48,19 @@ def _disassembly(tmp_path):
                        check=True, capture_output=True)
         dis = subprocess.run([_tool("llvm-objdump"), "-d", "--no-show-raw-insn", str(obj)],
                              check=True, capture_output=True, text=True).stdout
-        if f"<{KERNEL}>:" in dis:
+        if all(f"<{k}>:" in dis for k in KERNELS):
             return dis
-    pytest.fail("the dense anchor forward kernel is not in the library")
+    pytest.fail("the anchor forward kernels are not in the library")
 
 
-def test_half_precision_loop_placement(tmp_path):
-    dis = _disassembly(tmp_path)
+@pytest.fixture(scope="module")
+def disassembly(tmp_path_factory):
+    return _disassembly(tmp_path_factory.mktemp("code"))
+
+
+@pytest.mark.parametrize("KERNEL", KERNELS, ids=["forward", "gradient_preparation"])
+def test_half_precision_loop_placement(disassembly, KERNEL):
+    dis = disassembly
     head = re.search(r"^([0-9a-f]+) <" + re.escape(KERNEL) + ">:$", dis, re.M)
     base = int(head.group(1), 16)
     body = dis[head.end():].split("\n\n")[0].splitlines()
