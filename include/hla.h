@@ -331,10 +331,11 @@ hla_status hla_softmax_anchor_lse(hla_dtype dt, int B, int N, int H, int D,
  *   dg_i = dO_i y_i s_i (1 - s_i),  dY_i = dO_i s_i,  dP_ij = dY_i . v_j
  *   Delta_i = dY_i . y_i,  dL_ij = p_ij (dP_ij - Delta_i)
  *   dq_i = scale sum_j dL_ij k_j,  dk_j = scale sum_i dL_ij q_i,  dv_j = sum_i p_ij dY_i
- * The forward is recomputed (a pass that also yields each row's normaliser),
- * nothing of it is kept. q, k, v, g, dO, dq, dk, dv, dg: [B][N][H][D] bf16;
- * dg must be given exactly when g is. Products run on bf16 matrix cores with
- * float accumulation; p, dL and dY are rounded to bf16 as product operands.
+ * The forward is recomputed (a pass that also yields each row's normaliser,
+ * with the score forms of hla_softmax_anchor), nothing of it is kept. q, k, v,
+ * g, dO, dq, dk, dv, dg: [B][N][H][D] bf16; dg must be given exactly when g
+ * is. The gradient products run on bf16 matrix cores with float accumulation;
+ * p, dL and dY are rounded to bf16 as product operands.
  * No atomics: repeated calls are bitwise identical.
  * ws: at least hla_softmax_anchor_backward_workspace(B, N, H, D) bytes.
  * Errors: as hla_softmax_anchor, plus INVALID_ARG for null dO/dq/dk/dv or a
