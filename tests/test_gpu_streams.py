@@ -5,7 +5,7 @@ library call is issued on that side stream with no other synchronisation. Had
 any kernel run on another stream it would read the inputs before they exist
 (they start as uninitialised memory); on the given stream it reads them in
 order, and the outputs equal those of the same call on the default stream
-bitwise. Streams keep the default priority.
+bitwise. Streams keep the default priority. Forward calls and gradients.
 """
 import pytest
 import torch
@@ -67,3 +67,24 @@ def test_anchor_and_route_on_a_side_stream():
         h, al = hla.hla_attnres_route(xs[4:], w, None, alpha=True, stream=side)
     side.synchronize()
     assert torch.equal(o, ref) and torch.equal(h, ref_h) and torch.equal(al, ref_a)
+
+
+def test_gradients_on_a_side_stream():
+    say("[streams] linear and anchor gradients")
+    x = [dev(synth.randn(954, (B, N, H, 64), stream=i)) for i in range(5)]
+    q, k, v, g, do = x
+    rope = hla.Rope3D(GRID)
+    ref_l = hla.hla_linear_attn_backward(q, k, v, do, g, rope)
+    ref_c = hla.hla_linear_attn_chunked_backward(q, k, v, do, 300, g, rope)[:4]
+    ref_a = hla.hla_softmax_anchor_backward(q, k, v, do, g)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    qs, ks, vs, gs, ds = delayed_copies(side, x)
+    with torch.cuda.stream(side):
+        gl = hla.hla_linear_attn_backward(qs, ks, vs, ds, gs, rope, stream=side)
+        gc = hla.hla_linear_attn_chunked_backward(qs, ks, vs, ds, 300, gs, rope, stream=side)[:4]
+        ga = hla.hla_softmax_anchor_backward(qs, ks, vs, ds, gs, stream=side)
+    side.synchronize()
+    for got, ref in ((gl, ref_l), (gc, ref_c), (ga, ref_a)):
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)
