@@ -35,7 +35,9 @@
  *   frees or synchronises, and keeps no pointer after it returns.
  * - Asynchrony: every call enqueues its kernels on `stream` (NULL = the
  *   default stream) and returns; outputs are valid once the stream has
- *   executed them.
+ *   executed them. A call enqueues kernels only (no memset or copy), so it can
+ *   be captured in a HIP graph and replayed; workspace contents on entry never
+ *   matter.
  * - Errors: arguments are validated before anything is launched. A rejected
  *   call returns HLA_ERR_INVALID_ARG, HLA_ERR_UNSUPPORTED or HLA_ERR_WORKSPACE
  *   and has no side effect. A failed launch returns HLA_ERR_HIP. No C++
