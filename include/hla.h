@@ -41,8 +41,10 @@
  * - Errors: arguments are validated before anything is launched. A rejected
  *   call returns HLA_ERR_INVALID_ARG, HLA_ERR_UNSUPPORTED or HLA_ERR_WORKSPACE
  *   and has no side effect. A failed launch returns HLA_ERR_HIP. No C++
- *   exception crosses this interface. The library holds no mutable global
- *   state, so calls from several host threads are safe.
+ *   exception crosses this interface. Apart from hla_linear_attn_noalloc's
+ *   static device array (see there) and caches of read-only device facts, the
+ *   library holds no mutable global state, so calls from several host threads
+ *   are safe.
  * - Aliasing: outputs must not overlap inputs, except kv_out == kv_in and
  *   ksum_out == ksum_in in hla_linear_attn_chunked and hla_linear_attn_causal,
  *   and dkv_in == dkv_out, dksum_in == dksum_out in
