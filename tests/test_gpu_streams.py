@@ -5,7 +5,8 @@ library call is issued on that side stream with no other synchronisation. Had
 any kernel run on another stream it would read the inputs before they exist
 (they start as uninitialised memory); on the given stream it reads them in
 order, and the outputs equal those of the same call on the default stream
-bitwise. Streams keep the default priority. Forward calls and gradients.
+bitwise. Streams keep the default priority. Forward calls and gradients, and
+calls from four host threads at once.
 """
 import pytest
 import torch
@@ -88,3 +89,39 @@ def test_gradients_on_a_side_stream():
     for got, ref in ((gl, ref_l), (gc, ref_c), (ga, ref_a)):
         for a, b in zip(got, ref):
             assert torch.equal(a, b)
+
+
+def test_calls_from_several_host_threads():
+    """Four host threads, each with its own stream, outputs and workspaces, call the linear layer and the
+    anchor at once; every result equals the same call made alone."""
+    import threading
+
+    say("[streams] four host threads")
+    xs = [[dev(synth.randn(955 + t, (B, N, H, 64), stream=i)) for i in range(4)] for t in range(4)]
+    rope = hla.Rope3D(GRID)
+    refs = []
+    for x in xs:
+        refs.append((hla.hla_linear_attn(*x, rope), hla.hla_softmax_anchor(*x)))
+    torch.cuda.synchronize()
+    got = [None] * 4
+    errors = []
+
+    def work(t):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                o = hla.hla_linear_attn(*xs[t], rope, stream=st)
+                oa = hla.hla_softmax_anchor(*xs[t], stream=st)
+            st.synchronize()
+            got[t] = (o, oa)
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for (o, oa), (r, ra) in zip(got, refs):
+        assert torch.equal(o, r) and torch.equal(oa, ra)
