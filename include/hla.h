@@ -131,7 +131,11 @@ hla_status hla_rope_table_host(int len, int pos0, int d_band, double base, float
  * q, k, v, g, o: [B][N][H][D] of dtype `dt` (token-major, head, then dim).
  * g may be NULL (no gate); rope may be NULL (no rotation).
  * ws: device workspace of at least hla_linear_attn_workspace(B, N, H, D) bytes
- *     (its contents on entry do not matter and are overwritten).
+ *     (its contents on entry do not matter and are overwritten). The split of
+ *     the sequence into work-group slabs, and so the workspace size, is planned
+ *     for 512 resident work-groups (two per CU on the 256 CUs of an MI355X), a
+ *     fixed figure so that the size query needs no device; on another part the
+ *     results are the same and only the schedule differs.
  * Errors: INVALID_ARG for null q/k/v/o, B, N or H <= 0, bad rope fields or a
  * rope grid whose product differs from N; UNSUPPORTED for D != 64 or an
  * unknown dtype; WORKSPACE if ws is NULL or ws_bytes is too small.
