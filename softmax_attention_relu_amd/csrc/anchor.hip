@@ -24,11 +24,10 @@
 //              scale log2(e), so the weights are exp2 of the products with no
 //              per-score arithmetic before the exponential.
 // At most 128 registers per lane keep every accumulator in VGPRs with four
-// waves per SIMD; the tile's row max is combined across the two lane halves
-// with v_permlane32_swap. On this chip the plain vector ALU work of the
-// softmax (one FMA, one max and half a conversion per score) does not overlap
-// the matrix-core work much, while exponentials largely do; that, not the
-// matrix cores, sets the kernel's speed.
+// waves per SIMD; on the running-max path the tile's row max is combined
+// across the two lane halves with v_permlane32_swap. The softmax's vector work
+// overlaps the matrix-core work of other waves only in part; that, not the
+// matrix cores alone, sets the kernel's speed.
 // The running max is refreshed lazily: rows keep their reference max until a
 // tile exceeds it by more than 8 (log2 units), so exponentials stay <= 2^8
 // and the O / row-sum rescale is almost never taken. The normaliser uses the
@@ -48,7 +47,7 @@ constexpr int kKRow = kD + 8;      // bf16 per LDS row of K (144 bytes)
 constexpr int kVRow = kBK + 8;     // bf16 per LDS row of V^T (144 bytes)
 constexpr int kORow = kD + 8;      // bf16 per LDS row of the output stage (144 bytes)
 constexpr float kLazy = 8.0f;      // lazy max threshold, log2 units
-constexpr float kStatic = 48.0f;   // largest static row reference, log2 units
+constexpr float kStatic = 48.0f;   // largest static logit bound b_i, log2 units
 // bounds for the half-precision scores: c |q_i| <= 2^10, |k_j|^2 <= 2^20, |v| <= 2^40
 constexpr float kHalfQ = 1024.0f;
 constexpr float kHalfK2 = 1048576.0f;
@@ -81,7 +80,7 @@ struct VtArgs {
   uint16_t *vt;  // [B*H][64][npad]
   int N, H, npad;
   // optional: the largest squared norm of the K rows of each 64-key block,
-  // [B*H][npad / 64] (the forward's static row reference)
+  // [B*H][npad / 64] (the forward's static logit bound)
   const uint16_t *k;
   float *kmax2;
   // optional with kmax2: the largest finite |v| element of each 64-key block
@@ -191,7 +190,7 @@ struct FwdArgs {
   uint16_t *o;
   int N, H, npad;
   float c;  // scale * log2(e)
-  // static row reference (nullable): the largest squared K norm of each 64-key
+  // static logit bound (nullable): the largest squared K norm of each 64-key
   // block of the head, [B*H][npad / 64]
   const float *kmax2;
   // half-precision scores (nullable, with kmax2): the largest finite |v| of each
