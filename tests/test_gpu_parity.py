@@ -290,6 +290,19 @@ def test_anchor_half_and_bf16_score_paths(q_std):
     assert not torch.equal(big_k, half)
 
 
+@pytest.mark.parametrize("scale", [0.01, 0.0625, 0.5, 2.0])
+def test_anchor_scales(scale):
+    """Scales other than 1/sqrt(D): small ones keep the static bound (half-precision scores), large
+    ones exceed it (running max); each against the oracle at that scale."""
+    x = {nm: synth.randn(620, (1, 1500, 2, 64), stream=i) for i, nm in enumerate("qkvg")}
+    d = {k: dev(v) for k, v in x.items()}
+    got = host(hla.hla_softmax_anchor(d["q"], d["k"], d["v"], d["g"], scale))
+    torch.cuda.synchronize()
+    f = {k: synth.to_f64(v) for k, v in x.items()}
+    ref = oracle.softmax_anchor(f["q"], f["k"], f["v"], f["g"], scale=scale)
+    assert normwise(got, ref) <= TOL_BF16
+
+
 def test_anchor_full_size_sampled_rows():
     w = synth.HYBRID_ANCHOR
     say(f"[parity] {w.name}: N={w.N} H={w.H}")
