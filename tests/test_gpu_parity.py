@@ -303,6 +303,25 @@ def test_anchor_scales(scale):
     assert normwise(got, ref) <= TOL_BF16
 
 
+def test_anchor_loops_mixed_in_one_call():
+    """One call whose work-groups take different loops: head 0 all half precision; in head 1 the rows
+    600-649 are scaled by 8 (beyond the static bound), so only the 512-row work-group holding them takes
+    the running max; head 2's values are scaled by 2^44 (beyond the |v| bound), all running max. Every
+    head against the oracle."""
+    x = {nm: synth.randn(630, (1, 1200, 3, 64), stream=i) for i, nm in enumerate("qkvg")}
+    f = {k: synth.to_f64(v) for k, v in x.items()}
+    f["q"][:, 600:650, 1] *= 8.0
+    f["v"][:, :, 2] *= 2.0 ** 44
+    d = {k: dev(v) for k, v in x.items()}  # the same power-of-two factors, exact in bf16
+    d["q"][:, 600:650, 1] *= 8.0
+    d["v"][:, :, 2] *= 2.0 ** 44
+    got = host(hla.hla_softmax_anchor(d["q"], d["k"], d["v"], d["g"], 0.125))
+    torch.cuda.synchronize()
+    ref = oracle.softmax_anchor(f["q"], f["k"], f["v"], f["g"], scale=0.125)
+    for h in range(3):
+        assert normwise(got[:, :, h], ref[:, :, h]) <= TOL_BF16, h
+
+
 def test_anchor_full_size_sampled_rows():
     w = synth.HYBRID_ANCHOR
     say(f"[parity] {w.name}: N={w.N} H={w.H}")
