@@ -664,16 +664,6 @@ struct BwdArgs {
   float c, scale;
 };
 
-// 16 bytes at p, or zeros when ok is false (p is then not read). Written as a
-// branch on purpose: a select between the loaded value and a named zero vector
-// can be turned into a load through a selected pointer, which puts the zero
-// vector (and the staged tile) in scratch memory.
-__device__ __forceinline__ uint4 chunk_or_zero(const uint16_t *p, bool ok) {
-  uint4 w = make_uint4(0, 0, 0, 0);
-  if (ok) w = *reinterpret_cast<const uint4 *>(p);
-  return w;
-}
-
 // B operands of 32 tokens' rows: lane (tl, half) holds token n (its wave's
 // token tl), dims 16 s + 8 half .. +7 (zero past N)
 __device__ __forceinline__ void row_operands(const uint16_t *base, size_t stride, int n, int half, int N,
@@ -700,14 +690,47 @@ __device__ __forceinline__ void store_cols(uint16_t *base, size_t stride, int n,
     }
 }
 
+// Tiles of the gradient kernels go global -> LDS directly (no staging registers):
+// rows of 128 bytes, unpadded, with row r's 16-byte chunk c in slot
+// c ^ ((r >> 1) & 7). An operand read serves 16 lanes (16 rows, one chunk
+// column) per pass over the 64 banks of 4 bytes; two consecutive rows fill one
+// 256-byte bank line, so rows 2m and 2m + 1 take its two halves and the eight
+// values of m take eight different slots: the 16 rows hit 64 different banks.
+// One copy instruction moves 8 rows (64 lanes x 16 bytes).
+__device__ __forceinline__ void copy_rows(const uint16_t *src, uint16_t *lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// A pointer the compiler keeps in scalar registers (p is the same in every lane).
+__device__ __forceinline__ const uint16_t *wave_uniform(const uint16_t *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint16_t *>(((uint64_t)hi << 32) | lo);
+}
+// The same copy from a wave-uniform base (a buffer resource in scalar
+// registers) plus this lane's byte offset, which then takes one vector
+// register instead of a 64-bit address.
+__device__ __forceinline__ void copy_rows_from(const uint16_t *base, uint32_t byte_off, uint16_t *lds) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, byte_off, 0, 0, 0);
+}
+
 template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 2) void anchor_dkdv_kernel(BwdArgs a) {
-  static_assert(64 * WAVES == kBK * 8, "one 16-byte chunk of each tile per thread");
-  __shared__ __align__(16) uint16_t qs[2][kBK * kKRow];  // Q rows of the query tile
-  __shared__ __align__(16) uint16_t ds[2][kBK * kKRow];  // dY rows
-  __shared__ __align__(16) uint16_t qts[2][kD * kVRow];  // Q^T, permuted
-  __shared__ __align__(16) uint16_t dts[2][kD * kVRow];  // dY^T, permuted
-  __shared__ __align__(16) float ls[2][kBK], dls[2][kBK];
+__global__ __launch_bounds__(64 * WAVES, 3) void anchor_dkdv_kernel(BwdArgs a) {
+  static_assert(WAVES == 12, "waves 0-7 copy the four tiles, waves 8 and 9 the row statistics");
+  // one block, row statistics first: a read's 16-bit immediate offset reaches
+  // the first 64 KB
+  struct Lds {
+    float ls[2][kBK], dls[2][kBK];  // L and -Delta of the tile's queries
+    uint16_t qs[2][kBK * kD];       // Q rows of the query tile
+    uint16_t ds[2][kBK * kD];       // dY rows
+    uint16_t qts[2][kD * kBK];      // Q^T, permuted
+    uint16_t dts[2][kD * kBK];      // dY^T, permuted
+  };
+  __shared__ __align__(16) Lds sm;
+  auto &ls = sm.ls, &dls = sm.dls;
+  auto &qs = sm.qs, &ds = sm.ds, &qts = sm.qts, &dts = sm.dts;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -721,36 +744,77 @@ __global__ __launch_bounds__(64 * WAVES, 2) void anchor_dkdv_kernel(BwdArgs a) {
   bf16x8_t kb[4], vb[4];
   row_operands(a.k + head_base, tok_stride, k0 + tl, half, a.N, kb);
   row_operands(a.v + head_base, tok_stride, k0 + tl, half, a.N, vb);
-  const uint16_t *qp = a.q + head_base, *dp = a.dy + head_base;
-  const uint16_t *qtp = a.qt + (size_t)bh * kD * a.npad, *dtp = a.dyt + (size_t)bh * kD * a.npad;
+  const uint16_t *qp = wave_uniform(a.q + head_base), *dp = wave_uniform(a.dy + head_base);
+  const uint16_t *qtp = wave_uniform(a.qt + (size_t)bh * kD * a.npad);
+  const uint16_t *dtp = wave_uniform(a.dyt + (size_t)bh * kD * a.npad);
   const float *lsp = a.lse + (size_t)bh * a.N, *dlp = a.delta + (size_t)bh * a.N;
 
-  const int row = tid >> 3, ch = tid & 7;
-  uint4 sreg[4];
+  // copier: wave w < 8 copies rows 32 (w % 2) .. +31 of tile w / 2 (Q, dY, Q^T,
+  // dY^T) in four instructions of 8 rows; lane i takes row + i / 8 and fills
+  // slot i % 8 with chunk (i % 8) ^ ((row >> 1) & 7), which is the lane's chunk
+  // of instruction 0 for even instructions and that ^ 4 for odd ones. Waves 8
+  // and 9 load L and -Delta of the next tile into a register.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int kind = wv >> 1, grp = 4 * (wv & 1);
+  const int crow = 8 * grp + (lane >> 3);  // + 8 i
+  const int cchunk = (lane & 7) ^ ((crow >> 1) & 7);
+  // row tiles: byte offsets of instructions 0 and 1 from the tile's first row
+  // (2 and 3 add 16 rows through the scalar offset)
+  const uint32_t roff0 = 2 * ((uint32_t)crow * (uint32_t)tok_stride + 8 * cchunk);
+  const uint32_t roff1 = 2 * ((uint32_t)(crow + 8) * (uint32_t)tok_stride + 8 * (cchunk ^ 4));
+  const uint16_t *rsrc = kind == 0 ? qp : dp;
+  // transposed tiles: this lane's pointers for instructions 0 and 1
+  const uint16_t *tsrc = kind == 2 ? qtp : dtp;
+  const uint16_t *tp0 = tsrc + (size_t)crow * a.npad + 8 * cchunk;
+  const uint16_t *tp1 = tsrc + (size_t)(crow + 8) * a.npad + 8 * (cchunk ^ 4);
+  const int ntiles = (a.N + kBK - 1) / kBK;
   float sf = 0.f;
-  auto load_tile = [&](int t) {
-    const int n0 = t * kBK, n = n0 + row;
-    sreg[0] = chunk_or_zero(qp + (size_t)n * tok_stride + 8 * ch, n < a.N);
-    sreg[1] = chunk_or_zero(dp + (size_t)n * tok_stride + 8 * ch, n < a.N);
-    sreg[2] = *reinterpret_cast<const uint4 *>(qtp + (size_t)row * a.npad + n0 + 8 * ch);
-    sreg[3] = *reinterpret_cast<const uint4 *>(dtp + (size_t)row * a.npad + n0 + 8 * ch);
-    // past N: a weight of exactly 0 and no Delta (waves 0 and 1 read L and Delta)
-    const int qn = n0 + (tid & (kBK - 1));
-    if (tid < kBK) {
-      sf = INFINITY;
-      if (qn < a.N) sf = lsp[qn];
-    } else if (tid < 2 * kBK) {
-      sf = 0.f;
-      if (qn < a.N) sf = dlp[qn];
+  auto issue_tile = [&](int t, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int n0 = t * kBK;
+    // every wave loads one value per lane (waves 8 and 9 keep L and Delta; rows
+    // past N read row N - 1): one definition on every path, applied when stored
+    sf = (wv == 8 ? lsp : dlp)[min(n0 + lane, a.N - 1)];
+    if (wv < 4) {
+      uint16_t *dst = kind == 0 ? qs[buf] : ds[buf];
+      const uint16_t *base = wave_uniform(rsrc + (size_t)n0 * tok_stride);
+      const uint32_t skip = 2 * 16 * (uint32_t)tok_stride;  // 16 rows, in bytes
+      if (n0 + kBK <= a.N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, -1,
+                                                                             0x00020000);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 512 * (grp + i)),
+                                                   16, (i & 1) ? roff1 : roff0, (i >> 1) * skip, 0, 0);
+        }
+      } else {
+        // rows past the end copy row N - 1: finite data, weight 0
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t r = (uint32_t)min(crow + 8 * i, a.N - 1 - n0);
+          copy_rows_from(base, 2 * (r * (uint32_t)tok_stride + 8 * (cchunk ^ (4 * (i & 1)))), dst + 512 * (grp + i));
+        }
+      }
+    } else if (wv < 8) {
+      uint16_t *dst = kind == 2 ? qts[buf] : dts[buf];
+      const size_t skip = (size_t)16 * a.npad;  // 16 rows
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        copy_rows(((i & 1) ? tp1 : tp0) + (i >> 1) * skip + n0, dst + 512 * (grp + i));
     }
   };
-  auto store_tile = [&](int buf) {
-    *reinterpret_cast<uint4 *>(&qs[buf][row * kKRow + 8 * ch]) = sreg[0];
-    *reinterpret_cast<uint4 *>(&ds[buf][row * kKRow + 8 * ch]) = sreg[1];
-    *reinterpret_cast<uint4 *>(&qts[buf][row * kVRow + 8 * ch]) = sreg[2];
-    *reinterpret_cast<uint4 *>(&dts[buf][row * kVRow + 8 * ch]) = sreg[3];
-    if (tid < 2 * kBK) (tid < kBK ? ls : dls)[buf][tid & (kBK - 1)] = sf;
+  // past N: a weight of exactly 0 and no Delta
+  auto store_stats = [&](int t, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const bool live = t * kBK + lane < a.N;
+    if (wv == 8) ls[buf][lane] = live ? sf : INFINITY;
+    if (wv == 9) dls[buf][lane] = live ? -sf : 0.f;
   };
+  // this lane's operand rows tl (+ 32 per block): chunk 2j + half sits in slot
+  // (2j + half) ^ ((tl >> 1) & 7); byte offsets within a tile
+  uint32_t roff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) roff[j] = 2 * (tl * kD + 8 * ((2 * j + half) ^ ((tl >> 1) & 7)));
 
   f32x16_t dva[2], dka[2];
 #pragma unroll
@@ -758,71 +822,85 @@ __global__ __launch_bounds__(64 * WAVES, 2) void anchor_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dva[mb][i] = dka[mb][i] = 0.f;
 
-  const int ntiles = (a.N + kBK - 1) / kBK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    // scores and dP of the tile's 64 queries (rows) against the wave's 32 keys
-    f32x16_t sacc[2], pacc[2];
+  // one tile of queries from buffer buf (a compile-time constant, so every LDS
+  // address is a lane offset plus an immediate); its two 32-query blocks one
+  // after the other
+  auto tile = [&](int t, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    // the other buffers held tile t - 1, whose readers all passed the last barrier
+    if (t + 1 < ntiles) issue_tile(t + 1, std::integral_constant<int, buf ^ 1>{});
+    const char *qbase = reinterpret_cast<const char *>(qs[buf]);
+    const char *dbase = reinterpret_cast<const char *>(ds[buf]);
+    const char *qtbase = reinterpret_cast<const char *>(qts[buf]);
+    const char *dtbase = reinterpret_cast<const char *>(dts[buf]);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      // scores and dP - Delta of 32 queries (rows) against the wave's 32 keys;
+      // the dP products accumulate onto -Delta of their rows
+      f32x16_t sacc, pacc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[qb][i] = pacc[qb][i] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const f32x4_t nd = *reinterpret_cast<const f32x4_t *>(&dls[buf][32 * qb + 8 * i + 4 * half]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sacc[4 * i + j] = 0.f;
+          pacc[4 * i + j] = nd[j];
+        }
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int off = (32 * qb + tl) * kKRow + 16 * s + 8 * half;
-        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&qs[buf][off]), kb[s],
-                                                           sacc[qb], 0, 0, 0);
-        pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&ds[buf][off]), vb[s],
-                                                           pacc[qb], 0, 0, 0);
+        const uint32_t off = 2 * 32 * qb * kD + roff[s];
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(qbase + off), kb[s], sacc,
+                                                       0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(dbase + off), vb[s], pacc,
+                                                       0, 0, 0);
       }
-    }
-    // weights and logit gradients: lane rows 32 qb + 8 i + 4 half + j
-    bf16x8_t pw[2][2], sw[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+      // weights and logit gradients: lane rows 32 qb + 8 i + 4 half + j
       float pv[16], dv[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4_t L = *reinterpret_cast<const f32x4_t *>(&ls[buf][32 * qb + 8 * i + 4 * half]);
-        const f32x4_t Dl = *reinterpret_cast<const f32x4_t *>(&dls[buf][32 * qb + 8 * i + 4 * half]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float pj = __builtin_amdgcn_exp2f(fmaf(sacc[qb][4 * i + j], a.c, -L[j]));
+          const float pj = __builtin_amdgcn_exp2f(fmaf(sacc[4 * i + j], a.c, -L[j]));
           pv[4 * i + j] = pj;
-          dv[4 * i + j] = pj * (pacc[qb][4 * i + j] - Dl[j]);
+          dv[4 * i + j] = pj * pacc[4 * i + j];
         }
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        pw[qb][u] = __builtin_bit_cast(
+        const bf16x8_t pw = __builtin_bit_cast(
             bf16x8_t, make_uint4(pack_bf16(pv[8 * u], pv[8 * u + 1]), pack_bf16(pv[8 * u + 2], pv[8 * u + 3]),
                                  pack_bf16(pv[8 * u + 4], pv[8 * u + 5]), pack_bf16(pv[8 * u + 6], pv[8 * u + 7])));
-        sw[qb][u] = __builtin_bit_cast(
+        const bf16x8_t sw = __builtin_bit_cast(
             bf16x8_t, make_uint4(pack_bf16(dv[8 * u], dv[8 * u + 1]), pack_bf16(dv[8 * u + 2], dv[8 * u + 3]),
                                  pack_bf16(dv[8 * u + 4], dv[8 * u + 5]), pack_bf16(dv[8 * u + 6], dv[8 * u + 7])));
+        // dV^T += dY^T P and dK^T += Q^T dS over these 16 queries: rows 32 mb + tl,
+        // columns 32 qb + 16 u + 8 half (chunk 4 qb + 2 u + half)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const uint32_t off = 2 * 32 * mb * kBK + roff[2 * qb + u];
+          dva[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(dtbase + off), pw,
+                                                            dva[mb], 0, 0, 0);
+          dka[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(qtbase + off), sw,
+                                                            dka[mb], 0, 0, 0);
+        }
       }
     }
-    // dV^T += dY^T P and dK^T += Q^T dS over the tile's queries
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int off = (32 * mb + tl) * kVRow + 32 * qb + 16 * u + 8 * half;
-          dva[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&dts[buf][off]),
-                                                            pw[qb][u], dva[mb], 0, 0, 0);
-          dka[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&qts[buf][off]),
-                                                            sw[qb][u], dka[mb], 0, 0, 0);
-        }
     if (t + 1 < ntiles) {
-      store_tile(buf ^ 1);  // the other buffer was last read two tiles ago
+      store_stats(t + 1, std::integral_constant<int, buf ^ 1>{});
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t + 1 has landed
       __syncthreads();
     }
+  };
+
+  issue_tile(0, std::integral_constant<int, 0>{});
+  store_stats(0, std::integral_constant<int, 0>{});
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
   const int n = k0 + tl;
   if (n < a.N) {
@@ -831,18 +909,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void anchor_dkdv_kernel(BwdArgs a) {
   }
 }
 
-// Tiles of the dq kernel go global -> LDS directly (no staging registers):
-// rows of 128 bytes, unpadded, with row r's 16-byte chunk c in slot c ^ (r & 7),
-// so the 8 rows that one operand read touches per chunk column fall in 8
-// different slots. One copy instruction moves 8 rows (64 lanes x 16 bytes).
-__device__ __forceinline__ void copy_rows(const uint16_t *src, uint16_t *lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-}
-
 template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
-  static_assert(WAVES == 16, "waves 0-7 copy K and V rows, waves 8-15 copy K^T rows");
+__global__ __launch_bounds__(64 * WAVES, 3) void anchor_dq_kernel(BwdArgs a) {
+  static_assert(WAVES == 12, "waves 0-3 copy K rows, 4-7 V rows, 8-11 K^T rows, 16 rows each");
   __shared__ __align__(16) uint16_t ks[2][kBK * kD];   // K rows of the key tile
   __shared__ __align__(16) uint16_t vr[2][kBK * kD];   // V rows
   __shared__ __align__(16) uint16_t kts[2][kD * kBK];  // K^T, permuted
@@ -861,68 +930,91 @@ __global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
   row_operands(a.dy + head_base, tok_stride, q0 + tl, half, a.N, db);
   const int nq = min(q0 + tl, a.N - 1);
   const float L = a.lse[(size_t)bh * a.N + nq], Dl = a.delta[(size_t)bh * a.N + nq];
-  const uint16_t *kp = a.k + head_base, *vp = a.v + head_base;
-  const uint16_t *ktp = a.kt + (size_t)bh * kD * a.npad;
+  const uint16_t *kp = wave_uniform(a.k + head_base), *vp = wave_uniform(a.v + head_base);
+  const uint16_t *ktp = wave_uniform(a.kt + (size_t)bh * kD * a.npad);
 
-  // copier: wave w copies rows 8 (w % 8) .. +7; lane i takes row + i / 8 and
-  // fills slot i % 8 with chunk (i % 8) ^ (row & 7)
+  // copier: wave w copies rows 16 (w % 4) .. +15 of tile w / 4 (K, V, K^T) in
+  // two instructions of 8 rows; lane i takes row + i / 8 and fills slot i % 8
+  // with chunk (i % 8) ^ ((row >> 1) & 7). Each tile's source is a wave-uniform
+  // base plus this lane's byte offset.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int crow = 8 * (wv & 7) + (lane >> 3);
-  const int cchunk = (lane & 7) ^ (crow & 7);
-  auto issue_tile = [&](int t, int buf) {
+  const int kind = wv >> 2, grp = 2 * (wv & 3);
+  const int crow = 8 * grp + (lane >> 3);  // and crow + 8
+  const int cchunk = (lane & 7) ^ ((crow >> 1) & 7), cchunk1 = cchunk ^ 4;
+  const uint32_t off0 = 2 * ((uint32_t)crow * (uint32_t)tok_stride + 8 * cchunk);
+  const uint32_t off1 = 2 * ((uint32_t)(crow + 8) * (uint32_t)tok_stride + 8 * cchunk1);
+  const uint16_t *src = kind == 0 ? kp : vp;
+  const uint16_t *kt0 = ktp + (size_t)crow * a.npad + 8 * cchunk, *kt1 = ktp + (size_t)(crow + 8) * a.npad + 8 * cchunk1;
+  const int ntiles = (a.N + kBK - 1) / kBK;
+  auto issue_tile = [&](int t, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     const int n0 = t * kBK;
-    if (wv < 8) {
-      const int n = min(n0 + crow, a.N - 1);  // rows past the end: finite data, weight 0
-      copy_rows(kp + (size_t)n * tok_stride + 8 * cchunk, &ks[buf][512 * wv]);
-      copy_rows(vp + (size_t)n * tok_stride + 8 * cchunk, &vr[buf][512 * wv]);
+    uint16_t *dst = kind == 0 ? ks[buf] : kind == 1 ? vr[buf] : kts[buf];
+    if (kind == 2) {
+      copy_rows(kt0 + n0, dst + 512 * grp);
+      copy_rows(kt1 + n0, dst + 512 * (grp + 1));
     } else {
-      copy_rows(ktp + (size_t)crow * a.npad + n0 + 8 * cchunk, &kts[buf][512 * (wv - 8)]);
+      // rows past the end copy row N - 1: finite data, weight 0
+      uint32_t o0 = off0, o1 = off1;
+      if (n0 + kBK > a.N) {
+        o0 = 2 * ((uint32_t)min(crow, a.N - 1 - n0) * (uint32_t)tok_stride + 8 * cchunk);
+        o1 = 2 * ((uint32_t)min(crow + 8, a.N - 1 - n0) * (uint32_t)tok_stride + 8 * cchunk1);
+      }
+      const uint16_t *base = wave_uniform(src + (size_t)n0 * tok_stride);
+      copy_rows_from(base, o0, dst + 512 * grp);
+      copy_rows_from(base, o1, dst + 512 * (grp + 1));
     }
   };
-  // this lane's operand rows tl (+ 32 per block): chunk 2j + half sits in slot (2j + half) ^ (tl & 7)
-  int roff[4];
+  // this lane's operand rows tl (+ 32 per block): chunk 2j + half sits in slot
+  // (2j + half) ^ ((tl >> 1) & 7); byte offsets within a tile
+  uint32_t roff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) roff[j] = tl * kD + 8 * ((2 * j + half) ^ (tl & 7));
+  for (int j = 0; j < 4; ++j) roff[j] = 2 * (tl * kD + 8 * ((2 * j + half) ^ ((tl >> 1) & 7)));
 
-  f32x16_t dqa[2];
+  f32x16_t dqa[2], ndl;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqa[mb][i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndl[i] = -Dl;
 
-  const int ntiles = (a.N + kBK - 1) / kBK;
-  issue_tile(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  // one tile of keys from buffer buf (a compile-time constant, so every LDS
+  // address is a lane offset plus an immediate)
+  auto tile = [&](int t, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     // the other buffers held tile t - 1, whose readers all passed the last barrier
-    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+    if (t + 1 < ntiles) issue_tile(t + 1, std::integral_constant<int, buf ^ 1>{});
     const bool tail = (t + 1) * kBK > a.N;
+    const char *kbase = reinterpret_cast<const char *>(ks[buf]);
+    const char *vbase = reinterpret_cast<const char *>(vr[buf]);
+    const char *tbase = reinterpret_cast<const char *>(kts[buf]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // S^T and dP^T of 32 of the tile's keys (rows) against the wave's 32 queries
-      f32x16_t sacc, pacc;
+      // S^T and dP^T - Delta of 32 of the tile's keys (rows) against the wave's
+      // 32 queries: the dP products accumulate onto -Delta of their columns
+      f32x16_t sacc, pacc = ndl;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int off = 32 * kb * kD + roff[s];
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&ks[buf][off]), qb[s], sacc,
+        const uint32_t off = 2 * 32 * kb * kD + roff[s];
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(kbase + off), qb[s], sacc,
                                                        0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&vr[buf][off]), db[s], pacc,
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(vbase + off), db[s], pacc,
                                                        0, 0, 0);
       }
       float dv[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int e = 0; e < 16; ++e) dv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e], a.c, -L));
+      // only a tile that reaches past N has keys to mask (weight 0)
+      if (__builtin_expect(tail, 0)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * i + j;
-          float pj = __builtin_amdgcn_exp2f(fmaf(sacc[e], a.c, -L));
-          if (tail && t * kBK + 32 * kb + 8 * i + 4 * half + j >= a.N) pj = 0.f;
-          dv[e] = pj * (pacc[e] - Dl);
-        }
+        for (int e = 0; e < 16; ++e)
+          if (t * kBK + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3) >= a.N) dv[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dv[e] *= pacc[e];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const bf16x8_t sw = __builtin_bit_cast(
@@ -931,8 +1023,8 @@ __global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
         // dQ^T += K^T dS^T over these keys
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const int off = 32 * mb * kBK + roff[2 * kb + u];
-          dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(&kts[buf][off]), sw,
+          const uint32_t off = 2 * 32 * mb * kBK + roff[2 * kb + u];
+          dqa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(tbase + off), sw,
                                                             dqa[mb], 0, 0, 0);
         }
       }
@@ -941,6 +1033,14 @@ __global__ __launch_bounds__(64 * WAVES, 4) void anchor_dq_kernel(BwdArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t + 1 has landed
       __syncthreads();
     }
+  };
+
+  issue_tile(0, std::integral_constant<int, 0>{});
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
   const int n = q0 + tl;
   if (n < a.N) store_cols(a.dq + head_base, tok_stride, n, half, dqa, a.scale);
@@ -1127,13 +1227,13 @@ hipError_t launch_anchor_backward(const AnchorBwdArgs &a, hipStream_t stream) {
   ba.npad = npad;
   ba.c = fa.c;
   ba.scale = a.scale;
-  constexpr int kBwdWaves = 8;
+  constexpr int kBwdWaves = 12;
   const dim3 grid((a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves), heads);
   hipLaunchKernelGGL((anchor_dkdv_kernel<kBwdWaves>), grid, dim3(64 * kBwdWaves), 0, stream, ba);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // dq: the tile's two 32-key blocks one after the other keep it within 128
-  // registers, so it runs sixteen waves (four per SIMD) like the forward
-  constexpr int kDqWaves = 16;
+  // dq: the tile's two 32-key blocks one after the other; twelve waves, three
+  // per SIMD
+  constexpr int kDqWaves = 12;
   hipLaunchKernelGGL((anchor_dq_kernel<kDqWaves>), dim3((a.N + 32 * kDqWaves - 1) / (32 * kDqWaves), heads),
                      dim3(64 * kDqWaves), 0, stream, ba);
   return hipGetLastError();
