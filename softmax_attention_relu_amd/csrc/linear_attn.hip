@@ -984,7 +984,8 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
     // shared by q, k, v, g and o (one layout); keeps 64-bit lane addresses out
     // of the step's registers
     const size_t step_base = head_base + (size_t)sub * tok_stride;
-    const uint32_t roff = (uint32_t)(min(n, hi - 1) - sub) * (uint32_t)(tok_stride * sizeof(uint16_t));
+    const int row = min(tl, hi - 1 - sub);  // rows past the end read the last one
+    const uint32_t roff = (uint32_t)row * (uint32_t)(tok_stride * sizeof(uint16_t));
     auto at = [&](const uint16_t *base, int d) {
       return reinterpret_cast<const char *>(base + step_base) + roff + d * sizeof(uint16_t);
     };
@@ -1014,7 +1015,7 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
         for (int i = 0; i < 4; ++i) gws[mb][i] = *reinterpret_cast<const uint2 *>(at(a.g, 32 * mb + 8 * i + 4 * half));
     }
     TokenPos tp;
-    if constexpr (kRope) tp = token_pos(a.rope, (uint32_t)min(n, hi - 1));
+    if constexpr (kRope) tp = token_pos(a.rope, (uint32_t)(sub + row));
     if (!valid) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) vp[s] = make_uint4(0, 0, 0, 0);
@@ -1038,6 +1039,9 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
       oacc[1][i] = 0.f;
     }
     float den_in = 0.f;
+    // the key-sum slot this lane's butterfly result adds to, less 32 kb + 16 s2
+    const int zt = 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1);
+    const int zslot = 4 * half + (zt < 4 ? zt : 4 + zt);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kb = st >> 1, s2 = st & 1;
@@ -1087,9 +1091,9 @@ __global__ __launch_bounds__(256, 2) void la_causal_kernel(CausalArgs a) {
         }
         v[0] += dpp_f32<0x4E>(v[0]);  // lane bit 1
         v[0] += dpp_f32<0xB1>(v[0]);  // lane bit 0
-        // v[0] is the sum for value 4*bit4 + 2*bit3 + bit2 of this half
-        const int t = 4 * ((lane >> 4) & 1) + 2 * b3 + b2;
-        if ((lane & 3) == 0) zs[(t < 4 ? d0 + t : d0 + 4 + t)] += v[0];
+        // v[0] is the sum for value 4*bit4 + 2*bit3 + bit2 of this half, which
+        // sits at zs[d0 + zslot] (a lane offset plus this step's constant)
+        if ((lane & 3) == 0) zs[zslot + 32 * kb + 16 * s2] += v[0];
       }
       float qa[8], kc[8];
 #pragma unroll
