@@ -62,3 +62,19 @@ def test_anchor_at_max_batch_heads():
         ref = oracle.softmax_anchor(f["q"], f["k"], f["v"], f["g"], scale=0.125)
         assert normwise(o[:, :, h:h + 1], ref) <= TOL_BF16, h
     assert np.isfinite(o).all()
+
+
+def test_anchor_gradients_at_max_batch_heads():
+    B, N, H = 5, 70, PAIRS // 5
+    say(f"[limits] anchor gradients B={B} N={N} H={H}")
+    x = {nm: synth.randn(902, (B, N, H, 64), stream=i) for i, nm in enumerate(("q", "k", "v", "g", "do"))}
+    d = {k: dev(v) for k, v in x.items()}
+    out = [host(t) for t in hla.hla_softmax_anchor_backward(d["q"], d["k"], d["v"], d["do"], d["g"], 0.125)]
+    torch.cuda.synchronize()
+    for h in sampled(H):
+        f = heads_of(x, h)
+        ref = oracle.softmax_anchor_backward(f["q"], f["k"], f["v"], f["do"], f["g"], 0.125)
+        for i, nm in enumerate(("dq", "dk", "dv", "dg")):
+            assert normwise(out[i][:, :, h:h + 1], ref[i]) <= TOL_BF16, (nm, h)
+    for t in out:
+        assert np.isfinite(t).all()
